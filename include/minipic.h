@@ -1,0 +1,191 @@
+/*
+ * minipic.h - C ABI of libminipic.so: position-free paged prefill attention
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one of "MiniPIC: Flexible Position-Independent Caching in
+ * <100LOC" (Ordonez, Parnell):
+ *   - §3.2.1 (score equation): score(t, j) = (R_t q_t)^T (R_pi(j) k~_j) / sqrt(d).
+ *     The KV cache holds unrotated keys k~_j; pi(j) is the per-request logical
+ *     position of key j, so one physical block can serve many requests at
+ *     different offsets (§3.3.1, last paragraph).
+ *   - §3.2.2 (kernel modification): each gathered K tile is rotated inside the
+ *     attention kernel after a cos/sin table lookup at pi(j); V is unchanged.
+ *   - §3.1.1 (three user-facing primitives): padding, SSep and PDep shape the
+ *     block-level attention structure. This library takes that structure as
+ *     per-block descriptors (span id and PDEP / GLOBAL bits).
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller, unless a comment
+ *     says "host". The library never allocates or frees device memory, never
+ *     synchronises, and enqueues all work on `stream` (a hipStream_t passed as
+ *     void*; NULL means the default stream), so calls can be captured in a
+ *     HIP graph.
+ *   - Every argument check runs before the first HIP call: an invalid call
+ *     returns an error code without touching the GPU. Checks cover host
+ *     scalars and pointer presence only; device arrays are read only by the
+ *     kernels, which clamp out-of-range indices into bounds and then record
+ *     the violation in the workspace error word (see minipic_prefill_attn).
+ *   - On failure, minipic_last_error() returns a thread-local description.
+ */
+#ifndef MINIPIC_H
+#define MINIPIC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+#define MINIPIC_OK               0
+#define MINIPIC_ERR_INVALID_ARG  (-1)  /* null pointer, negative or inconsistent size */
+#define MINIPIC_ERR_UNSUPPORTED  (-2)  /* dtype, head_dim, block_size or GQA ratio not built */
+#define MINIPIC_ERR_WORKSPACE    (-3)  /* workspace smaller than minipic_workspace_size() */
+#define MINIPIC_ERR_HIP          (-4)  /* a HIP call or launch failed; see minipic_last_error() */
+
+/* Element types of q, k, v, out and the caches. */
+#define MINIPIC_F32   0
+#define MINIPIC_BF16  1
+
+/* Per-block descriptor bits (blk_flags). */
+#define MINIPIC_BLK_PDEP    1u  /* block belongs to a PDep segment: its tokens see every earlier token */
+#define MINIPIC_BLK_GLOBAL  2u  /* shared-prefix block: visible to every later token of the request */
+
+/* Call flags (minipic_prefill_attn / minipic_reference_prerotated). */
+#define MINIPIC_FLAG_ROTATE_Q  1u  /* q is unrotated; rotate each row by pi(its context index) */
+
+/* Bits of the workspace error word (first uint32_t of the workspace). */
+#define MINIPIC_EW_BLOCK   1u  /* a block_table entry was outside [0, num_blocks) */
+#define MINIPIC_EW_POS     2u  /* a logical position was outside [0, max_pos) */
+#define MINIPIC_EW_QCTX    4u  /* a q_ctx_idx entry was outside [0, ctx_len) */
+#define MINIPIC_EW_CTX     8u  /* ctx_len exceeded max_blocks_per_req * block_size */
+
+/*
+ * One batch of prefill requests. Host scalars plus device arrays.
+ *
+ * Request r owns context tokens 0 .. ctx_len[r]-1 (its context index order)
+ * laid out in logical blocks of `block_size` tokens; logical block b lives in
+ * physical cache block block_table[r][b]. Its query rows are rows
+ * q_indptr[r] .. q_indptr[r+1]-1 of q / out; row i is the token at context
+ * index q_ctx_idx[i]. Query rows need not be a contiguous suffix (a prompt can
+ * interleave cached and freshly computed spans).
+ *
+ * Visibility (the block structure of "MiniPIC ...", §3.1.1 and §3.3.1), for a
+ * query at context index c and a key at context index j, with bc = c / 16 and
+ * bj = j / 16:
+ *     j <= c  and  ( PDEP(bc)  or  GLOBAL(bj)  or  span_id[bj] == span_id[bc] )
+ * Contract: a span_id value names ONE contiguous run of blocks of a request
+ * (runs are found by scanning neighbours; a value that reappears after another
+ * value is a different, invisible span). Causality is by context index, not by
+ * logical position. Pad tokens are ordinary tokens.
+ */
+typedef struct minipic_batch {
+  int32_t num_reqs;            /* number of requests, >= 0 */
+  int32_t num_q_heads;         /* Hq */
+  int32_t num_kv_heads;        /* Hkv; Hq / Hkv must be 1, 2, 4 or 8 */
+  int32_t head_dim;            /* d: 64 or 128 */
+  int32_t block_size;          /* tokens per cache block: must be 16 */
+  int32_t max_blocks_per_req;  /* row stride of block_table / span_id / blk_flags */
+  int64_t total_q;             /* q_indptr[num_reqs] (host copy) */
+  int32_t max_q_len;           /* >= max_r (q_indptr[r+1] - q_indptr[r]) (host) */
+  int32_t max_ctx_len;         /* >= max_r ctx_len[r] (host); sizes the split-KV plan */
+  const int32_t* q_indptr;     /* [num_reqs + 1], ascending, q_indptr[0] = 0 */
+  const int32_t* q_ctx_idx;    /* [total_q] context index of each query row, ascending per request */
+  const int32_t* ctx_len;      /* [num_reqs] */
+  const int32_t* block_table;  /* [num_reqs][max_blocks_per_req] physical block ids */
+  const int32_t* logical_pos;  /* [num_reqs][max_blocks_per_req * block_size] pi per context token */
+  const int32_t* span_id;      /* [num_reqs][max_blocks_per_req] */
+  const uint8_t* blk_flags;    /* [num_reqs][max_blocks_per_req] MINIPIC_BLK_* bits */
+} minipic_batch;
+
+/* Launch geometry chosen for a batch (host-side planning, no GPU work). */
+typedef struct minipic_launch_info {
+  int32_t rows_per_tile;       /* query rows (token x head) per work-group */
+  int32_t tokens_per_tile;     /* query tokens per work-group */
+  int32_t num_q_tiles;         /* q tiles per request (upper bound) */
+  int32_t num_splits;          /* key-range splits per q tile (1 = no split-KV) */
+  int32_t split_blocks;        /* key blocks per split */
+  int32_t threads;             /* threads per work-group */
+  int64_t num_workgroups;      /* grid size of the attention kernel */
+} minipic_launch_info;
+
+const char* minipic_version(void);
+const char* minipic_status_string(int status);
+/* Thread-local text of the last failure on this thread ("" if none). */
+const char* minipic_last_error(void);
+
+/*
+ * Fill the cos/sin lookup table used by the in-kernel rotation ("MiniPIC ...",
+ * §3.2.2: a cos/sin table lookup per K element).
+ *   cos_sin : device float32 [max_pos][head_dim]; row p holds cos(p * theta_i)
+ *             in columns [0, d/2) and sin(p * theta_i) in columns [d/2, d),
+ *             with theta_i = base^(-2i/d) (rotate-half pairing i <-> i + d/2).
+ *             Angles and sin/cos are evaluated in float64 on the GPU and
+ *             rounded once to float32.
+ *   max_pos > 0, head_dim even (64 or 128 for the attention kernels), base > 0.
+ */
+int minipic_rope_table(float* cos_sin, int32_t max_pos, int32_t head_dim, double base,
+                       void* stream);
+
+/*
+ * Scatter the UNROTATED keys k~ and the values of new tokens into the paged
+ * cache by slot mapping ("MiniPIC ...", abstract and §3.2: the cache stores
+ * unrotated K vectors; V is stored as is).
+ *   k, v         : [num_tokens][num_kv_heads][head_dim], element type `dtype`
+ *   slot_mapping : int64 [num_tokens]; slot = physical_block * block_size + offset;
+ *                  a negative slot skips the token; a slot beyond the cache is
+ *                  skipped as well.
+ *   k_cache      : [num_blocks][num_kv_heads][block_size][head_dim]
+ *   v_cache      : [num_blocks][num_kv_heads][head_dim][block_size]  (V transposed
+ *                  inside each block, so attention reads key-contiguous V rows)
+ * Bits are copied exactly; no arithmetic is applied.
+ */
+int minipic_write_kv(const void* k, const void* v, const int64_t* slot_mapping, int64_t num_tokens,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                     void* k_cache, void* v_cache, int64_t num_blocks, int32_t dtype,
+                     void* stream);
+
+/* Bytes of device workspace minipic_prefill_attn needs for `batch` (host scalars only). */
+int minipic_workspace_size(const minipic_batch* batch, int32_t dtype, size_t* bytes);
+
+/* Launch geometry for `batch` (host scalars only; for tests and reporting). */
+int minipic_get_launch_info(const minipic_batch* batch, int32_t dtype, minipic_launch_info* info);
+
+/*
+ * Position-free paged prefill attention ("MiniPIC ...", §3.2.1 and §3.2.2).
+ *   q        : [total_q][num_q_heads][head_dim]; R_t q_t (already rotated by the
+ *              query's own logical position t = pi(c)) unless MINIPIC_FLAG_ROTATE_Q.
+ *   k_cache, v_cache : layouts of minipic_write_kv, holding UNROTATED keys.
+ *   num_blocks : physical blocks in each cache.
+ *   cos_sin  : float32 [max_pos][head_dim] as filled by minipic_rope_table.
+ *   softmax_scale : <= 0 means 1/sqrt(head_dim).
+ *   out      : [total_q][num_q_heads][head_dim], element type `dtype`.
+ *   workspace: device scratch of minipic_workspace_size() bytes (256-byte
+ *              aligned). Its first uint32_t is the error word: kernels OR in
+ *              MINIPIC_EW_* bits when they meet out-of-range metadata (after
+ *              clamping it); the caller may read it after its own sync and
+ *              should zero it to reset it. The library never reads it back.
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ */
+int minipic_prefill_attn(const void* q, const void* k_cache, const void* v_cache, int64_t num_blocks,
+                         const minipic_batch* batch, const float* cos_sin, int32_t max_pos,
+                         float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+                         uint32_t flags, int32_t dtype, void* stream);
+
+/*
+ * The same kernel without the in-kernel key rotation: k_cache holds keys that
+ * are ALREADY rotated (R_pi(j) k~_j), as in the baseline FlashAttention of
+ * "MiniPIC ...", §3.2.2. Used to measure the cost of the rotation. cos_sin /
+ * max_pos are needed only with MINIPIC_FLAG_ROTATE_Q (may be NULL / 0 otherwise).
+ */
+int minipic_reference_prerotated(const void* q, const void* k_cache, const void* v_cache,
+                                 int64_t num_blocks, const minipic_batch* batch,
+                                 const float* cos_sin, int32_t max_pos, float softmax_scale,
+                                 void* out, void* workspace, size_t workspace_bytes,
+                                 uint32_t flags, int32_t dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MINIPIC_H */

@@ -1,0 +1,160 @@
+"""ctypes binding of libminipic.so (argument marshalling only).
+
+Each function takes torch tensors that already live on the GPU, passes their
+data pointers and the current HIP stream to the C entry point of the same
+name, and raises MinipicError on a non-zero status. No arithmetic of the
+method happens here.
+"""
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libminipic.so")
+
+MINIPIC_OK = 0
+MINIPIC_ERR_INVALID_ARG = -1
+MINIPIC_ERR_UNSUPPORTED = -2
+MINIPIC_ERR_WORKSPACE = -3
+MINIPIC_ERR_HIP = -4
+MINIPIC_F32 = 0
+MINIPIC_BF16 = 1
+MINIPIC_BLK_PDEP = 1
+MINIPIC_BLK_GLOBAL = 2
+MINIPIC_FLAG_ROTATE_Q = 1
+MINIPIC_EW_BLOCK = 1
+MINIPIC_EW_POS = 2
+MINIPIC_EW_QCTX = 4
+MINIPIC_EW_CTX = 8
+
+EXPORTS = [
+    "minipic_version", "minipic_status_string", "minipic_last_error", "minipic_rope_table",
+    "minipic_write_kv", "minipic_workspace_size", "minipic_get_launch_info", "minipic_prefill_attn",
+    "minipic_reference_prerotated",
+]
+
+
+class MinipicError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"minipic status {status}: {msg}")
+        self.status = status
+
+
+class minipic_batch(ctypes.Structure):
+    _fields_ = [
+        ("num_reqs", ctypes.c_int32), ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32), ("max_blocks_per_req", ctypes.c_int32),
+        ("total_q", ctypes.c_int64), ("max_q_len", ctypes.c_int32), ("max_ctx_len", ctypes.c_int32),
+        ("q_indptr", ctypes.c_void_p), ("q_ctx_idx", ctypes.c_void_p), ("ctx_len", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p), ("logical_pos", ctypes.c_void_p), ("span_id", ctypes.c_void_p),
+        ("blk_flags", ctypes.c_void_p),
+    ]
+
+
+class minipic_launch_info(ctypes.Structure):
+    _fields_ = [
+        ("rows_per_tile", ctypes.c_int32), ("tokens_per_tile", ctypes.c_int32), ("num_q_tiles", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32), ("split_blocks", ctypes.c_int32), ("threads", ctypes.c_int32),
+        ("num_workgroups", ctypes.c_int64),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libminipic.so; fails loudly if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m position_independent_paged_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.minipic_version.restype = ctypes.c_char_p
+    lib.minipic_status_string.restype = ctypes.c_char_p
+    lib.minipic_status_string.argtypes = [ctypes.c_int]
+    lib.minipic_last_error.restype = ctypes.c_char_p
+    lib.minipic_rope_table.argtypes = [vp, i32, i32, ctypes.c_double, vp]
+    lib.minipic_write_kv.argtypes = [vp, vp, vp, i64, i32, i32, i32, vp, vp, i64, i32, vp]
+    lib.minipic_workspace_size.argtypes = [ctypes.POINTER(minipic_batch), i32, ctypes.POINTER(sz)]
+    lib.minipic_get_launch_info.argtypes = [ctypes.POINTER(minipic_batch), i32, ctypes.POINTER(minipic_launch_info)]
+    attn = [vp, vp, vp, i64, ctypes.POINTER(minipic_batch), vp, i32, ctypes.c_float, vp, vp, sz, ctypes.c_uint32,
+            i32, vp]
+    lib.minipic_prefill_attn.argtypes = attn
+    lib.minipic_reference_prerotated.argtypes = attn
+    for name in EXPORTS[3:]:
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != MINIPIC_OK:
+        lib = load_library()
+        raise MinipicError(status, lib.minipic_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream)
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return MINIPIC_BF16
+    if t.dtype == torch.float32:
+        return MINIPIC_F32
+    raise MinipicError(MINIPIC_ERR_UNSUPPORTED, f"unsupported tensor dtype {t.dtype}")
+
+
+def minipic_version() -> str:
+    return load_library().minipic_version().decode()
+
+
+def minipic_rope_table(cos_sin, max_pos: int, head_dim: int, base: float, stream=None):
+    _check(load_library().minipic_rope_table(_ptr(cos_sin), max_pos, head_dim, float(base), _stream(stream)))
+
+
+def minipic_write_kv(k, v, slot_mapping, k_cache, v_cache, *, num_kv_heads: int, head_dim: int,
+                     block_size: int = 16, num_blocks: int, stream=None):
+    _check(load_library().minipic_write_kv(
+        _ptr(k), _ptr(v), _ptr(slot_mapping), int(slot_mapping.shape[0]), num_kv_heads, head_dim, block_size,
+        _ptr(k_cache), _ptr(v_cache), int(num_blocks), _dtype_code(k_cache), _stream(stream)))
+
+
+def minipic_workspace_size(batch: minipic_batch, dtype_code: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().minipic_workspace_size(ctypes.byref(batch), dtype_code, ctypes.byref(n)))
+    return int(n.value)
+
+
+def minipic_get_launch_info(batch: minipic_batch, dtype_code: int) -> dict:
+    info = minipic_launch_info()
+    _check(load_library().minipic_get_launch_info(ctypes.byref(batch), dtype_code, ctypes.byref(info)))
+    return {f: getattr(info, f) for f, _ in minipic_launch_info._fields_}
+
+
+def _attn(fn, q, k_cache, v_cache, num_blocks, batch, cos_sin, max_pos, out, workspace, flags, softmax_scale,
+          stream):
+    _check(fn(_ptr(q), _ptr(k_cache), _ptr(v_cache), int(num_blocks), ctypes.byref(batch), _ptr(cos_sin),
+              int(max_pos), float(softmax_scale), _ptr(out), _ptr(workspace),
+              0 if workspace is None else workspace.numel() * workspace.element_size(), int(flags),
+              _dtype_code(q), _stream(stream)))
+
+
+def minipic_prefill_attn(q, k_cache, v_cache, num_blocks, batch, cos_sin, max_pos, out, workspace, *,
+                         flags: int = 0, softmax_scale: float = 0.0, stream=None):
+    _attn(load_library().minipic_prefill_attn, q, k_cache, v_cache, num_blocks, batch, cos_sin, max_pos, out,
+          workspace, flags, softmax_scale, stream)
+
+
+def minipic_reference_prerotated(q, k_cache, v_cache, num_blocks, batch, out, workspace, *, cos_sin=None,
+                                 max_pos: int = 0, flags: int = 0, softmax_scale: float = 0.0, stream=None):
+    _attn(load_library().minipic_reference_prerotated, q, k_cache, v_cache, num_blocks, batch, cos_sin, max_pos,
+          out, workspace, flags, softmax_scale, stream)

@@ -1,0 +1,295 @@
+// Host side of libminipic.so: argument validation, launch planning and
+// dispatch. Every check here reads host values only and runs before the first
+// HIP call, so a rejected call never touches the GPU.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+
+#include "../../include/minipic.h"
+#include "common.h"
+
+namespace minipic {
+hipError_t launch_attn_bf16(const AttnParams& p, int D, int G, bool rope, int64_t grid, hipStream_t s);
+hipError_t launch_attn_f32(const AttnParams& p, int D, int G, bool rope, int64_t grid, hipStream_t s);
+hipError_t launch_combine(const AttnParams& p, int D, int dtype, int bq, int G, int64_t grid, hipStream_t s);
+hipError_t launch_write_kv(const void* k, const void* v, const int64_t* slots, int64_t n, int hkv, int D,
+                           void* kc, void* vc, int64_t num_blocks, int dtype, hipStream_t s);
+hipError_t launch_rope_table(float* cs, int max_pos, int d, double base, hipStream_t s);
+}  // namespace minipic
+
+using namespace minipic;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(MINIPIC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool supported_dim(int d) { return d == 64 || d == 128; }
+bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
+
+struct Plan {
+  int rows, bq, nqt, splits, split_blocks, threads;
+  int64_t grid;
+  size_t off_nsplit, off_ml, off_o, bytes;
+};
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int check_batch(const minipic_batch* b, int dtype) {
+  if (!b) return fail(MINIPIC_ERR_INVALID_ARG, "batch is NULL");
+  if (dtype != MINIPIC_F32 && dtype != MINIPIC_BF16)
+    return fail(MINIPIC_ERR_UNSUPPORTED, "dtype %d is not MINIPIC_F32 or MINIPIC_BF16", dtype);
+  if (b->num_reqs < 0) return fail(MINIPIC_ERR_INVALID_ARG, "num_reqs < 0");
+  if (b->num_q_heads <= 0 || b->num_kv_heads <= 0)
+    return fail(MINIPIC_ERR_INVALID_ARG, "head counts must be positive");
+  if (b->num_q_heads % b->num_kv_heads != 0)
+    return fail(MINIPIC_ERR_UNSUPPORTED, "num_q_heads %% num_kv_heads != 0");
+  if (!supported_group(b->num_q_heads / b->num_kv_heads))
+    return fail(MINIPIC_ERR_UNSUPPORTED, "query heads per KV head must be 1, 2, 4 or 8 (got %d)",
+                b->num_q_heads / b->num_kv_heads);
+  if (!supported_dim(b->head_dim)) return fail(MINIPIC_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (b->block_size != kBlock) return fail(MINIPIC_ERR_UNSUPPORTED, "block_size must be 16");
+  if (b->max_blocks_per_req <= 0) return fail(MINIPIC_ERR_INVALID_ARG, "max_blocks_per_req must be > 0");
+  if (b->total_q < 0 || b->max_q_len < 0 || b->max_ctx_len < 0)
+    return fail(MINIPIC_ERR_INVALID_ARG, "negative size in batch");
+  if ((int64_t)b->max_ctx_len > (int64_t)b->max_blocks_per_req * kBlock)
+    return fail(MINIPIC_ERR_INVALID_ARG, "max_ctx_len exceeds max_blocks_per_req * block_size");
+  if (b->total_q > 0 && b->max_q_len == 0) return fail(MINIPIC_ERR_INVALID_ARG, "max_q_len is 0 but total_q > 0");
+  if (b->num_reqs > 0 && b->total_q > 0) {
+    if (!b->q_indptr || !b->q_ctx_idx || !b->ctx_len || !b->block_table || !b->logical_pos || !b->span_id ||
+        !b->blk_flags)
+      return fail(MINIPIC_ERR_INVALID_ARG, "a batch array pointer is NULL");
+  }
+  if (b->total_q > (int64_t)INT32_MAX) return fail(MINIPIC_ERR_INVALID_ARG, "total_q too large");
+  return MINIPIC_OK;
+}
+
+int env_int(const char* name, int dflt) {
+  const char* s = std::getenv(name);
+  if (!s || !*s) return dflt;
+  return std::atoi(s);
+}
+
+void make_plan(const minipic_batch* b, int dtype, Plan* p) {
+  const int G = b->num_q_heads / b->num_kv_heads;
+  if (dtype == MINIPIC_BF16) {
+    p->rows = 256;
+    p->threads = 512;
+  } else {
+    p->rows = 64;
+    p->threads = 256;
+  }
+  p->bq = p->rows / G;
+  p->nqt = b->max_q_len > 0 ? (b->max_q_len + p->bq - 1) / p->bq : 0;
+  const int nb_max = (b->max_ctx_len + kBlock - 1) / kBlock;
+  // Key splits: a q tile whose visible blocks exceed `split_blocks` is cut into
+  // up to `splits` pieces (long PDep rows next to short span rows).
+  int splits = env_int("MINIPIC_SPLITS", 8);
+  int min_chunk = env_int("MINIPIC_MIN_SPLIT_BLOCKS", 16);
+  if (splits < 1) splits = 1;
+  if (splits > 64) splits = 64;
+  if (min_chunk < 1) min_chunk = 1;
+  int chunk = nb_max > 0 ? (nb_max + splits - 1) / splits : 1;
+  if (chunk < min_chunk) chunk = min_chunk;
+  if (nb_max <= chunk) {
+    splits = 1;
+    chunk = nb_max > 0 ? nb_max : 1;
+  } else {
+    splits = (nb_max + chunk - 1) / chunk;
+  }
+  p->splits = splits;
+  p->split_blocks = chunk;
+  p->grid = (int64_t)b->num_reqs * p->nqt * b->num_kv_heads * splits;
+  size_t off = kAlign;  // error word
+  p->off_nsplit = off;
+  off = align_up(off + sizeof(int32_t) * (size_t)b->num_reqs * p->nqt * b->num_kv_heads);
+  p->off_ml = off;
+  if (splits > 1) {
+    off = align_up(off + sizeof(float) * 2 * (size_t)splits * b->total_q * b->num_q_heads);
+    p->off_o = off;
+    off = align_up(off + sizeof(float) * (size_t)splits * b->total_q * b->num_q_heads * b->head_dim);
+  } else {
+    p->off_o = off;
+  }
+  p->bytes = off;
+}
+
+int run_attention(const void* q, const void* k_cache, const void* v_cache, int64_t num_blocks,
+                  const minipic_batch* b, const float* cos_sin, int32_t max_pos, float softmax_scale,
+                  void* out, void* workspace, size_t workspace_bytes, uint32_t flags, int32_t dtype,
+                  void* stream, bool rope) {
+  int st = check_batch(b, dtype);
+  if (st) return st;
+  if (flags & ~(uint32_t)MINIPIC_FLAG_ROTATE_Q) return fail(MINIPIC_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
+  if (num_blocks < 0) return fail(MINIPIC_ERR_INVALID_ARG, "num_blocks < 0");
+  const bool need_table = rope || (flags & MINIPIC_FLAG_ROTATE_Q);
+  if (need_table) {
+    if (!cos_sin) return fail(MINIPIC_ERR_INVALID_ARG, "cos_sin is NULL");
+    if (max_pos <= 0) return fail(MINIPIC_ERR_INVALID_ARG, "max_pos must be > 0");
+  }
+  if (b->num_reqs == 0 || b->total_q == 0) return MINIPIC_OK;
+  if (!q || !out) return fail(MINIPIC_ERR_INVALID_ARG, "q or out is NULL");
+  if (!k_cache || !v_cache) return fail(MINIPIC_ERR_INVALID_ARG, "k_cache or v_cache is NULL");
+  if (num_blocks == 0) return fail(MINIPIC_ERR_INVALID_ARG, "num_blocks is 0");
+  if (!(softmax_scale == softmax_scale) || std::isinf(softmax_scale))
+    return fail(MINIPIC_ERR_INVALID_ARG, "softmax_scale is not finite");
+  Plan pl;
+  make_plan(b, dtype, &pl);
+  if (!workspace) return fail(MINIPIC_ERR_INVALID_ARG, "workspace is NULL");
+  if ((uintptr_t)workspace % kAlign) return fail(MINIPIC_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (workspace_bytes < pl.bytes)
+    return fail(MINIPIC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, pl.bytes);
+  if (pl.grid > (int64_t)INT32_MAX) return fail(MINIPIC_ERR_INVALID_ARG, "batch too large for one launch");
+
+  AttnParams P{};
+  P.q = q;
+  P.k_cache = k_cache;
+  P.v_cache = v_cache;
+  P.out = out;
+  P.cos_sin = cos_sin;
+  P.q_indptr = b->q_indptr;
+  P.q_ctx_idx = b->q_ctx_idx;
+  P.ctx_len = b->ctx_len;
+  P.block_table = b->block_table;
+  P.logical_pos = b->logical_pos;
+  P.span_id = b->span_id;
+  P.blk_flags = b->blk_flags;
+  char* ws = (char*)workspace;
+  P.err = (uint32_t*)ws;
+  P.tile_nsplit = (int32_t*)(ws + pl.off_nsplit);
+  P.part_ml = (float2*)(ws + pl.off_ml);
+  P.part_o = (float*)(ws + pl.off_o);
+  P.num_blocks = num_blocks;
+  P.total_q = b->total_q;
+  P.num_reqs = b->num_reqs;
+  P.hq = b->num_q_heads;
+  P.hkv = b->num_kv_heads;
+  P.max_blocks = b->max_blocks_per_req;
+  P.max_pos = need_table ? max_pos : 1;
+  P.num_q_tiles = pl.nqt;
+  P.num_splits = pl.splits;
+  P.split_blocks = pl.split_blocks;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)b->head_dim);
+  P.scale_log2 = scale * 1.4426950408889634f;
+  P.flags = flags;
+  const int G = b->num_q_heads / b->num_kv_heads;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = dtype == MINIPIC_BF16 ? launch_attn_bf16(P, b->head_dim, G, rope, pl.grid, s)
+                                       : launch_attn_f32(P, b->head_dim, G, rope, pl.grid, s);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  if (pl.splits > 1) {
+    const int64_t cgrid = (int64_t)b->num_reqs * pl.nqt * b->num_kv_heads;
+    e = launch_combine(P, b->head_dim, dtype, pl.bq, G, cgrid, s);
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+  }
+  return MINIPIC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* minipic_version(void) { return "minipic-mi355x 0.1.0 (gfx950)"; }
+
+const char* minipic_status_string(int status) {
+  switch (status) {
+    case MINIPIC_OK: return "ok";
+    case MINIPIC_ERR_INVALID_ARG: return "invalid argument";
+    case MINIPIC_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MINIPIC_ERR_WORKSPACE: return "workspace too small";
+    case MINIPIC_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* minipic_last_error(void) { return g_last_error.c_str(); }
+
+int minipic_rope_table(float* cos_sin, int32_t max_pos, int32_t head_dim, double base, void* stream) {
+  if (!cos_sin) return fail(MINIPIC_ERR_INVALID_ARG, "cos_sin is NULL");
+  if (max_pos <= 0) return fail(MINIPIC_ERR_INVALID_ARG, "max_pos must be > 0");
+  if (head_dim <= 0 || head_dim % 2) return fail(MINIPIC_ERR_INVALID_ARG, "head_dim must be even and > 0");
+  if (!(base > 0.0) || std::isinf(base)) return fail(MINIPIC_ERR_INVALID_ARG, "base must be finite and > 0");
+  hipError_t e = launch_rope_table(cos_sin, max_pos, head_dim, base, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "rope table launch");
+  return MINIPIC_OK;
+}
+
+int minipic_write_kv(const void* k, const void* v, const int64_t* slot_mapping, int64_t num_tokens,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, void* k_cache, void* v_cache,
+                     int64_t num_blocks, int32_t dtype, void* stream) {
+  if (dtype != MINIPIC_F32 && dtype != MINIPIC_BF16) return fail(MINIPIC_ERR_UNSUPPORTED, "unknown dtype %d", dtype);
+  if (num_tokens < 0) return fail(MINIPIC_ERR_INVALID_ARG, "num_tokens < 0");
+  if (num_kv_heads <= 0) return fail(MINIPIC_ERR_INVALID_ARG, "num_kv_heads must be > 0");
+  if (!supported_dim(head_dim)) return fail(MINIPIC_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (block_size != kBlock) return fail(MINIPIC_ERR_UNSUPPORTED, "block_size must be 16");
+  if (num_blocks < 0) return fail(MINIPIC_ERR_INVALID_ARG, "num_blocks < 0");
+  if (num_tokens == 0) return MINIPIC_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache) return fail(MINIPIC_ERR_INVALID_ARG, "NULL pointer");
+  if ((num_tokens + kBlock - 1) / kBlock > (int64_t)INT32_MAX) return fail(MINIPIC_ERR_INVALID_ARG, "too many tokens");
+  hipError_t e = launch_write_kv(k, v, slot_mapping, num_tokens, num_kv_heads, head_dim, k_cache, v_cache,
+                                 num_blocks, dtype, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "write_kv launch");
+  return MINIPIC_OK;
+}
+
+int minipic_workspace_size(const minipic_batch* batch, int32_t dtype, size_t* bytes) {
+  if (!bytes) return fail(MINIPIC_ERR_INVALID_ARG, "bytes is NULL");
+  int st = check_batch(batch, dtype);
+  if (st) return st;
+  Plan pl;
+  make_plan(batch, dtype, &pl);
+  *bytes = pl.bytes;
+  return MINIPIC_OK;
+}
+
+int minipic_get_launch_info(const minipic_batch* batch, int32_t dtype, minipic_launch_info* info) {
+  if (!info) return fail(MINIPIC_ERR_INVALID_ARG, "info is NULL");
+  int st = check_batch(batch, dtype);
+  if (st) return st;
+  Plan pl;
+  make_plan(batch, dtype, &pl);
+  info->rows_per_tile = pl.rows;
+  info->tokens_per_tile = pl.bq;
+  info->num_q_tiles = pl.nqt;
+  info->num_splits = pl.splits;
+  info->split_blocks = pl.split_blocks;
+  info->threads = pl.threads;
+  info->num_workgroups = pl.grid;
+  return MINIPIC_OK;
+}
+
+int minipic_prefill_attn(const void* q, const void* k_cache, const void* v_cache, int64_t num_blocks,
+                         const minipic_batch* batch, const float* cos_sin, int32_t max_pos, float softmax_scale,
+                         void* out, void* workspace, size_t workspace_bytes, uint32_t flags, int32_t dtype,
+                         void* stream) {
+  return run_attention(q, k_cache, v_cache, num_blocks, batch, cos_sin, max_pos, softmax_scale, out, workspace,
+                       workspace_bytes, flags, dtype, stream, /*rope=*/true);
+}
+
+int minipic_reference_prerotated(const void* q, const void* k_cache, const void* v_cache, int64_t num_blocks,
+                                 const minipic_batch* batch, const float* cos_sin, int32_t max_pos,
+                                 float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+                                 uint32_t flags, int32_t dtype, void* stream) {
+  return run_attention(q, k_cache, v_cache, num_blocks, batch, cos_sin, max_pos, softmax_scale, out, workspace,
+                       workspace_bytes, flags, dtype, stream, /*rope=*/false);
+}
+
+}  // extern "C"

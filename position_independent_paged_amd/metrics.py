@@ -1,0 +1,51 @@
+"""Host-side work accounting for a prefill batch (reporting only).
+
+Counts the visible (query, key) pairs of a batch from its per-block
+descriptors, walking runs of equal span id instead of evaluating a dense
+mask: a query at context index c whose block is PDep sees c + 1 keys; any
+other query sees the keys of its own run up to itself plus every key in a
+GLOBAL block of an earlier run ("MiniPIC: Flexible Position-Independent
+Caching in <100LOC", §3.1.1 and §3.3.1 for the meaning of the markers).
+
+Algorithmic FLOPs of attention = 4 * d * Hq * pairs (one multiply-add for
+QK^T and one for PV per pair and head dim element); exps, masking and the
+rotation are not counted.
+"""
+import numpy as np
+
+PDEP = 1
+GLOBAL = 2
+
+
+def visible_pairs(q_indptr, q_ctx_idx, ctx_len, span_id, blk_flags, block_size=16) -> int:
+    q_indptr = np.asarray(q_indptr, np.int64)
+    total = 0
+    for r in range(len(q_indptr) - 1):
+        qc = np.asarray(q_ctx_idx[q_indptr[r]:q_indptr[r + 1]], np.int64)
+        if len(qc) == 0:
+            continue
+        L = int(ctx_len[r])
+        nb = (L + block_size - 1) // block_size
+        sp = np.asarray(span_id[r][:nb])
+        fl = np.asarray(blk_flags[r][:nb]).astype(np.int64)
+        # run start of every block
+        starts = np.zeros(nb, np.int64)
+        for b in range(1, nb):
+            starts[b] = starts[b - 1] if sp[b] == sp[b - 1] else b
+        # tokens in GLOBAL blocks strictly before each block
+        tok_in_blk = np.minimum(block_size, L - np.arange(nb) * block_size)
+        glob_tok = np.concatenate([[0], np.cumsum(np.where(fl & GLOBAL, tok_in_blk, 0))])
+        bq = qc // block_size
+        pdep = (fl[bq] & PDEP) != 0
+        s0 = starts[bq]
+        own = qc - s0 * block_size + 1
+        total += int(np.where(pdep, qc + 1, own + glob_tok[s0]).sum())
+    return total
+
+
+def attention_flops(pairs: int, num_q_heads: int, head_dim: int) -> int:
+    return 4 * head_dim * num_q_heads * int(pairs)
+
+
+def workload_pairs(w) -> int:
+    return visible_pairs(w.q_indptr, w.q_ctx_idx, w.ctx_len, w.span_id, w.blk_flags, w.block_size)

@@ -1,0 +1,273 @@
+"""GPU parity of libminipic.so against the CPU oracle (needs an MI355X).
+
+Every call goes through the C ABI (ctypes binding). Tolerances: fp32
+workloads max |err| <= 1e-4; bf16 workloads max |err| <= 2e-2 and relative
+L2 error <= 1e-2, against the float64 oracle on the same inputs.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workload
+from workload import Segment
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def stage(w, **kw):
+    from position_independent_paged_amd.staging import DeviceWorkload
+    return DeviceWorkload(w, **kw)
+
+
+def out_f64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def check(name, got, want, dtype):
+    err = np.abs(got - want)
+    mx = float(err.max()) if err.size else 0.0
+    rel = float(np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-30)) if err.size else 0.0
+    say(f"  {name}: rows={got.shape[0]} max_abs={mx:.3e} rel_l2={rel:.3e}")
+    assert np.isfinite(got).all(), name
+    if dtype == "f32":
+        assert mx <= 1e-4, (name, mx)
+    else:
+        assert mx <= 2e-2 and rel <= 1e-2, (name, mx, rel)
+
+
+def compare_workload(w, out, rows_per_req=None, seed=0, q_rotated=True, k_rotated=False):
+    """Compare `out` [total_q, Hq, d] with the oracle, all rows or a sample per request."""
+    rng = np.random.default_rng(seed)
+    got_all, want_all = [], []
+    for r in range(w.num_reqs):
+        q0, q1 = int(w.q_indptr[r]), int(w.q_indptr[r + 1])
+        if q1 == q0:
+            continue
+        rows = np.arange(q1 - q0)
+        if rows_per_req is not None and len(rows) > rows_per_req:
+            # always include the last rows (longest context) and a spread of the rest
+            tail = rows[-min(64, rows_per_req // 2):]
+            rest = rng.choice(rows[:-len(tail)], rows_per_req - len(tail), replace=False)
+            rows = np.sort(np.concatenate([rest, tail]))
+        want_all.append(oracle.workload_reference(w, r, rows=rows, q_rotated=q_rotated, k_rotated=k_rotated))
+        got_all.append(out[q0 + rows])
+    return np.concatenate(got_all), np.concatenate(want_all)
+
+
+# ---------------------------------------------------------------------------
+# tables and cache writes
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d,base,max_pos", [(64, 1e4, 128), (128, 5e5, 32768)])
+def test_rope_table(d, base, max_pos):
+    import position_independent_paged_amd as pip
+    say(f"rope_table d={d} base={base} max_pos={max_pos}")
+    cs = torch.empty((max_pos, d), dtype=torch.float32, device="cuda")
+    pip.minipic_rope_table(cs, max_pos, d, base)
+    torch.cuda.synchronize()
+    ang = oracle.rope_angles(np.arange(max_pos), d, base)
+    want = np.concatenate([np.cos(ang), np.sin(ang)], axis=1)
+    got = cs.cpu().numpy().astype(np.float64)
+    assert np.abs(got - want).max() <= 6e-8
+
+
+@pytest.mark.parametrize("name", ["c1", "c3_small", "c5_small"])
+def test_write_kv_bit_exact(name):
+    w = workload.make_config(name)
+    say(f"write_kv {name}")
+    dw = stage(w)
+    dw.write_new()
+    torch.cuda.synchronize()
+    bits = np.uint16 if w.dtype == "bf16" else np.uint32
+    view = torch.int16 if w.dtype == "bf16" else torch.int32
+    kc = dw.k_cache.view(view).cpu().numpy().view(bits)
+    vc = dw.v_cache.view(view).cpu().numpy().view(bits)
+    ktok = np.asarray(w.k_tok).view(bits)
+    vtok = np.asarray(w.v_tok).view(bits)
+    # host scatter of every token (set-up and new) into the documented layouts
+    kref = np.zeros_like(kc)
+    vref = np.zeros_like(vc)
+    slots = w.tok_slot
+    blk, off = slots // 16, slots % 16
+    kref[blk, :, off, :] = ktok
+    vref[blk, :, :, off] = vtok
+    assert np.array_equal(kc, kref)
+    assert np.array_equal(vc, vref)
+
+
+def test_write_kv_scattered_and_skipped_slots():
+    """Tokens that do not fill a block in order take the element-wise path;
+    negative slots are skipped."""
+    rng = np.random.default_rng(11)
+    from position_independent_paged_amd import minipic_write_kv
+    n, hkv, d, nb = 45, 2, 128, 8
+    k = torch.from_numpy(rng.standard_normal((n, hkv, d), dtype=np.float32)).to(torch.bfloat16).cuda()
+    v = torch.from_numpy(rng.standard_normal((n, hkv, d), dtype=np.float32)).to(torch.bfloat16).cuda()
+    slots = rng.permutation(nb * 16)[:n].astype(np.int64)
+    slots[[3, 17, 40]] = -1
+    kc = torch.zeros((nb, hkv, 16, d), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros((nb, hkv, d, 16), dtype=torch.bfloat16, device="cuda")
+    say("write_kv scattered")
+    minipic_write_kv(k, v, torch.from_numpy(slots).cuda(), kc, vc, num_kv_heads=hkv, head_dim=d, num_blocks=nb)
+    torch.cuda.synchronize()
+    kr = torch.zeros_like(kc).cpu()
+    vr = torch.zeros_like(vc).cpu()
+    kh, vh = k.cpu(), v.cpu()
+    for t, s in enumerate(slots):
+        if s >= 0:
+            kr[s // 16, :, s % 16, :] = kh[t]
+            vr[s // 16, :, :, s % 16] = vh[t]
+    assert torch.equal(kc.cpu().view(torch.int16), kr.view(torch.int16))
+    assert torch.equal(vc.cpu().view(torch.int16), vr.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# attention parity
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["c1", "c1_cached", "c3_small", "c4_small", "c5_small", "c2", "c3"])
+def test_parity_all_rows(name):
+    w = workload.make_config(name)
+    say(f"parity {name}: dtype={w.dtype} R={w.num_reqs} total_q={w.total_q} max_ctx={w.max_ctx_len}")
+    dw = stage(w)
+    say(f"  plan {dw.launch_info()}")
+    dw.step()
+    torch.cuda.synchronize()
+    assert dw.error_word() == 0
+    got, want = compare_workload(w, out_f64(dw.out))
+    check(name, got, want, w.dtype)
+
+
+@pytest.mark.parametrize("name,rows", [("c4", 384), ("c5", 96)])
+def test_parity_sampled_full_size(name, rows):
+    w = workload.make_config(name)
+    say(f"parity(sampled) {name}: total_q={w.total_q} max_ctx={w.max_ctx_len}")
+    dw = stage(w)
+    say(f"  plan {dw.launch_info()}")
+    dw.step()
+    torch.cuda.synchronize()
+    assert dw.error_word() == 0
+    got, want = compare_workload(w, out_f64(dw.out), rows_per_req=rows, seed=1)
+    check(name, got, want, w.dtype)
+
+
+@pytest.mark.parametrize("name", ["c1", "c3_small", "c5_small"])
+def test_prerotated_kernel_parity(name):
+    """The pre-rotated variant treats the cached keys as already rotated."""
+    w = workload.make_config(name)
+    say(f"prerotated {name}")
+    dw = stage(w)
+    dw.write_new()
+    dw.attend_prerotated()
+    torch.cuda.synchronize()
+    got, want = compare_workload(w, out_f64(dw.out), k_rotated=True)
+    check(name + "/prerot", got, want, w.dtype)
+
+
+@pytest.mark.parametrize("name", ["c1", "c3_small"])
+def test_rotate_q_flag(name):
+    import position_independent_paged_amd as pip
+    w = workload.make_config(name)
+    say(f"rotate_q {name}")
+    dw = stage(w, flags=pip.MINIPIC_FLAG_ROTATE_Q)
+    dw.step()
+    torch.cuda.synchronize()
+    got, want = compare_workload(w, out_f64(dw.out), q_rotated=False)
+    check(name + "/rotq", got, want, w.dtype)
+
+
+def _variant(dtype, G, d, seed, positions_shift=0, nreq=2):
+    Hkv = 2
+    rng = np.random.default_rng(seed)
+    reqs = []
+    for r in range(nreq):
+        segs = [Segment("global", 32, fresh=False, pool=0)] if r % 2 else []
+        segs += [Segment("span", 16 * int(rng.integers(1, 9))) for _ in range(3)]
+        segs += [Segment("span", 48, fresh=False, pool=1)]
+        segs += [Segment("pdep", int(rng.integers(5, 70)))]
+        reqs.append(segs)
+    pos = None
+    w0 = workload.custom("v", reqs, pool_lengths=[32, 48], num_q_heads=Hkv * G, num_kv_heads=Hkv, head_dim=d,
+                         dtype=dtype, rope_theta=1e4 if d == 64 else 5e5, max_pos=8192, seed=seed)
+    if positions_shift:
+        pos = [np.arange(int(L), dtype=np.int32) + positions_shift for L in w0.ctx_len]
+        w0 = workload.custom("v", reqs, pool_lengths=[32, 48], num_q_heads=Hkv * G, num_kv_heads=Hkv,
+                             head_dim=d, dtype=dtype, rope_theta=1e4 if d == 64 else 5e5, max_pos=8192,
+                             seed=seed, positions=pos)
+    return w0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("d", [64, 128])
+def test_parity_heads_and_dims(dtype, G, d):
+    w = _variant(dtype, G, d, seed=G * 100 + d)
+    say(f"variant dtype={dtype} G={G} d={d} total_q={w.total_q}")
+    dw = stage(w)
+    dw.step()
+    torch.cuda.synchronize()
+    assert dw.error_word() == 0
+    got, want = compare_workload(w, out_f64(dw.out))
+    check(f"{dtype}/G{G}/d{d}", got, want, dtype)
+
+
+def test_shifted_positions():
+    """Logical positions far from the context index (a span reused late in a
+    long prompt); with Q rotated in-kernel by its own position the output
+    matches the oracle, which depends only on position differences."""
+    import position_independent_paged_amd as pip
+    w = _variant("bf16", 4, 128, seed=5, positions_shift=6000)
+    say("shifted positions")
+    dw = stage(w, flags=pip.MINIPIC_FLAG_ROTATE_Q)
+    dw.step()
+    torch.cuda.synchronize()
+    got, want = compare_workload(w, out_f64(dw.out), q_rotated=False)
+    check("shift6000", got, want, "bf16")
+
+
+def test_edge_layouts():
+    """A request with no query rows, one single-token request, the same pool
+    span twice in one request, queries that are not a suffix, and a ragged
+    final block."""
+    reqs = [
+        [Segment("span", 64, fresh=False, pool=0)],                                   # no queries
+        [Segment("pdep", 1)],                                                          # single token
+        [Segment("span", 64, fresh=False, pool=0), Segment("span", 32), Segment("span", 64, fresh=False, pool=0),
+         Segment("span", 48), Segment("pdep", 23)],                                    # same blocks twice
+        [Segment("span", 16), Segment("span", 96, fresh=False), Segment("span", 80), Segment("pdep", 7)],
+    ]
+    for dtype in ("bf16", "f32"):
+        w = workload.custom("edge", reqs, pool_lengths=[64], num_q_heads=8, num_kv_heads=2, head_dim=128,
+                            dtype=dtype, rope_theta=5e5, max_pos=4096, seed=9)
+        say(f"edge layouts {dtype} q_indptr={w.q_indptr.tolist()}")
+        dw = stage(w)
+        dw.step()
+        torch.cuda.synchronize()
+        assert dw.error_word() == 0
+        got, want = compare_workload(w, out_f64(dw.out))
+        check(f"edge/{dtype}", got, want, dtype)
+
+
+def test_deterministic():
+    w = workload.make_config("c4_small")
+    say("determinism c4_small")
+    dw = stage(w)
+    dw.step()
+    a = dw.out.clone()
+    dw.attend()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), dw.out.view(torch.int16))

@@ -1,0 +1,174 @@
+"""CPU-only checks of the library boundary and host logic (no GPU needed).
+
+The library must load and export every entry point declared in
+include/minipic.h; every invalid call must be rejected by host-side checks
+before any HIP call is made.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import workload
+import position_independent_paged_amd as pip
+from position_independent_paged_amd import metrics
+from position_independent_paged_amd._binding import minipic_batch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "minipic.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(minipic_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_header_symbol():
+    lib = ctypes.CDLL(pip.LIB_PATH)
+    names = header_functions()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(names) == sorted(pip.EXPORTS)
+
+
+def test_version_and_status_strings():
+    lib = pip.load_library()
+    assert b"gfx950" in lib.minipic_version()
+    assert lib.minipic_status_string(0) == b"ok"
+    assert lib.minipic_status_string(-3) == b"workspace too small"
+
+
+def _batch(**kw):
+    d = dict(num_reqs=1, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, max_blocks_per_req=10,
+             total_q=100, max_q_len=100, max_ctx_len=160, q_indptr=8, q_ctx_idx=8, ctx_len=8, block_table=8,
+             logical_pos=8, span_id=8, blk_flags=8)
+    d.update(kw)
+    return minipic_batch(**d)
+
+
+def _attn(b, dtype=1, ws_bytes=1 << 30, q=256, out=256, ws=256, table=256, max_pos=1024, flags=0, rope=True):
+    lib = pip.load_library()
+    fn = lib.minipic_prefill_attn if rope else lib.minipic_reference_prerotated
+    return fn(q, 256, 256, 10, ctypes.byref(b), table, max_pos, 0.0, out, ws, ws_bytes, flags, dtype, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=96), -2),
+    (dict(num_q_heads=12, num_kv_heads=8), -2),
+    (dict(num_q_heads=48, num_kv_heads=4), -2),      # 12 heads per group
+    (dict(block_size=32), -2),
+    (dict(num_reqs=-1), -1),
+    (dict(max_blocks_per_req=0), -1),
+    (dict(max_ctx_len=161), -1),
+    (dict(total_q=-5), -1),
+    (dict(q_indptr=None), -1),
+    (dict(max_q_len=0), -1),
+])
+def test_attention_rejects_bad_batch(kw, code):
+    assert _attn(_batch(**kw)) == code
+    assert pip.load_library().minipic_last_error()
+
+
+def test_attention_rejects_bad_buffers():
+    b = _batch()
+    assert _attn(b, dtype=7) == -2
+    assert _attn(b, q=None) == -1
+    assert _attn(b, table=None) == -1
+    assert _attn(b, max_pos=0) == -1
+    assert _attn(b, flags=0x10) == -1
+    assert _attn(b, ws=None) == -1
+    assert _attn(b, ws=256 + 4) == -1                 # misaligned
+    assert _attn(b, ws_bytes=64) == -3
+    # the pre-rotated variant does not need the table
+    assert _attn(b, table=None, max_pos=0, ws_bytes=64, rope=False) == -3
+
+
+def test_empty_batch_is_a_no_op():
+    # nothing to compute: returns before any HIP call
+    assert _attn(_batch(total_q=0, max_q_len=0)) == 0
+    assert _attn(_batch(num_reqs=0, total_q=0, max_q_len=0)) == 0
+
+
+def test_write_kv_validation():
+    lib = pip.load_library()
+    wk = lambda **kw: lib.minipic_write_kv(*[kw.get(k, v) for k, v in [
+        ("k", 256), ("v", 256), ("slots", 256), ("n", 10), ("hkv", 8), ("d", 128), ("bs", 16), ("kc", 256),
+        ("vc", 256), ("nb", 4), ("dtype", 1), ("stream", None)]])
+    assert wk(bs=8) == -2
+    assert wk(d=80) == -2
+    assert wk(dtype=3) == -2
+    assert wk(n=-1) == -1
+    assert wk(hkv=0) == -1
+    assert wk(k=None) == -1
+    assert wk(n=0) == 0
+
+
+def test_rope_table_validation():
+    lib = pip.load_library()
+    assert lib.minipic_rope_table(None, 10, 128, 1e4, None) == -1
+    assert lib.minipic_rope_table(256, 0, 128, 1e4, None) == -1
+    assert lib.minipic_rope_table(256, 10, 127, 1e4, None) == -1
+    assert lib.minipic_rope_table(256, 10, 128, -1.0, None) == -1
+
+
+def test_launch_plan_and_workspace():
+    b = _batch(total_q=15872, max_q_len=15872, max_ctx_len=31232, max_blocks_per_req=1952)
+    info = pip.minipic_get_launch_info(b, 1)
+    assert info["tokens_per_tile"] == 64 and info["rows_per_tile"] == 256
+    assert info["num_q_tiles"] == 248
+    assert info["num_splits"] * info["split_blocks"] >= 1952
+    ws = pip.minipic_workspace_size(b, 1)
+    S = info["num_splits"]
+    assert ws >= S * 15872 * 32 * (128 + 2) * 4
+    # short contexts are not split
+    small = _batch(total_q=80, max_q_len=80, max_ctx_len=80, max_blocks_per_req=5, num_q_heads=4,
+                   num_kv_heads=2, head_dim=64)
+    assert pip.minipic_get_launch_info(small, 0)["num_splits"] == 1
+
+
+@pytest.mark.parametrize("name", ["c1", "c1_cached", "c3_small", "c4_small", "c5_small", "c2"])
+def test_pair_counter_matches_oracle_mask(name):
+    w = workload.make_config(name)
+    assert metrics.workload_pairs(w) == oracle.visible_pair_count(w)
+
+
+def test_pair_counts_of_benchmark_layouts():
+    # analytic counts of the layouts: c2 = sys 512 causal + 10 spans of 192 + PDep 64 over 2432..2495
+    w = workload.make_config("c2")
+    tri = lambda n: n * (n + 1) // 2
+    want = tri(512) + 10 * tri(192) + sum(2432 + i + 1 for i in range(64))
+    assert metrics.workload_pairs(w) == want
+    w4 = workload.make_config("c4")
+    want4 = 60 * tri(256) + sum(30720 + i + 1 for i in range(512))
+    assert metrics.workload_pairs(w4) == want4
+
+
+def test_generator_layout_invariants():
+    w = workload.make_config("c3")
+    # same pool span -> same physical blocks in two requests at different offsets
+    seen = {}
+    for r in range(w.num_reqs):
+        for s0, seg in zip(w.seg_start[r], w.segments[r]):
+            if seg.pool is None:
+                continue
+            blocks = tuple(w.block_table[r, s0 // 16:(s0 + seg.length) // 16])
+            seen.setdefault(seg.pool, set()).add(blocks)
+    assert all(len(v) == 1 for v in seen.values())
+    # every physical block is used by one allocation only
+    assert len(np.unique(w.tok_slot)) == len(w.tok_slot)
+    # the draw is deterministic
+    w2 = workload.make_config("c3")
+    assert np.array_equal(w.q, w2.q) and np.array_equal(w.block_table, w2.block_table)
+
+
+def test_bf16_rounding_is_rne():
+    x = np.array([1.0, 1.00390625, 1.01171875, -2.5, 3.0e38, np.inf], np.float32)
+    # 1 + 2^-8 is a tie between 1 and 1 + 2^-7: rounds to even (1.0)
+    b = workload.f32_to_bf16_bits(x)
+    back = workload.bf16_bits_to_f32(b)
+    assert back[0] == 1.0 and back[1] == 1.0 and back[2] == 1.015625 and back[3] == -2.5
+    assert np.isinf(back[5])
