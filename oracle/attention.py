@@ -65,12 +65,12 @@ def prefill_attention(q, q_ctx, k, v, pos, span_id, flags, *, block_size: int, t
         m = block_mask(q_ctx[r0:r1], L, span_id, flags, block_size)       # [n, L]
         for g in range(Hkv):
             qg = q[r0:r1, g * G:(g + 1) * G, :]                             # [n, G, d]
-            s = np.einsum("ngd,ld->ngl", qg, kr[:, g, :]) * scale          # [n, G, L]
+            s = np.matmul(qg, kr[:, g, :].T) * scale                        # [n, G, L]
             s = np.where(m[:, None, :], s, -np.inf)
             mx = s.max(axis=-1, keepdims=True)
             p = np.exp(s - mx)
             p /= p.sum(axis=-1, keepdims=True)
-            out[r0:r1, g * G:(g + 1) * G, :] = np.einsum("ngl,ld->ngd", p, v[:, g, :])
+            out[r0:r1, g * G:(g + 1) * G, :] = np.matmul(p, v[:, g, :])     # [n, G, d]
     return out
 
 

@@ -1,8 +1,9 @@
 """Position-free paged prefill attention for AMD Instinct MI355X (gfx950).
 
 The compute path is libminipic.so (HIP C++, see include/minipic.h); this
-package is its thin Python binding plus device staging helpers. Importing it
-loads the library and fails loudly if it has not been built.
+package is its thin Python binding plus device staging helpers. The library
+is loaded on the first call into it (or by ``load_library()``), which raises
+ImportError if it has not been built: there is no fallback path.
 """
 from ._binding import (EXPORTS, MINIPIC_BF16, MINIPIC_BLK_GLOBAL, MINIPIC_BLK_PDEP, MINIPIC_EW_BLOCK,
                        MINIPIC_EW_CTX, MINIPIC_EW_POS, MINIPIC_EW_QCTX, MINIPIC_F32, MINIPIC_FLAG_ROTATE_Q,
@@ -10,7 +11,6 @@ from ._binding import (EXPORTS, MINIPIC_BF16, MINIPIC_BLK_GLOBAL, MINIPIC_BLK_PD
                        minipic_prefill_attn, minipic_reference_prerotated, minipic_rope_table,
                        minipic_version, minipic_workspace_size, minipic_write_kv)
 
-load_library()
 
 __all__ = [
     "EXPORTS", "LIB_PATH", "MinipicError", "load_library", "minipic_batch", "minipic_get_launch_info",

@@ -38,12 +38,16 @@ FLAG_GLOBAL = 2
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 to bfloat16 with round-to-nearest-even; returns uint16 bits."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    u = x.view(np.uint32)
+    # u + 0x7FFF + lsb cannot wrap for any non-NaN input (largest: 0xFF800000 + 0x8000)
+    t = (u >> 16) & np.uint32(1)
+    t += u
+    t += np.uint32(0x7FFF)
+    t >>= 16
+    r = t.astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
-        r = np.where(nan, np.uint16(0x7FC0), r)
+        r[nan] = np.uint16(0x7FC0)
     return r
 
 
@@ -149,7 +153,8 @@ class Workload:
         span = self.span_id[r, :nb].astype(np.int64)
         flags = self.blk_flags[r, :nb].astype(np.int64)
         q0, q1 = int(self.q_indptr[r]), int(self.q_indptr[r + 1])
-        q = self.q_f64()[q0:q1] if q1 > q0 else np.zeros((0, self.num_q_heads, self.head_dim))
+        q = self.as_f32(self.q[q0:q1]).astype(np.float64) if q1 > q0 else \
+            np.zeros((0, self.num_q_heads, self.head_dim))
         qc = self.q_ctx_idx[q0:q1].astype(np.int64)
         return dict(q=q, q_ctx=qc, k=k, v=v, pos=pos, span_id=span, flags=flags)
 
