@@ -94,20 +94,24 @@ typedef struct minipic_batch {
   const int32_t* q_ctx_idx;    /* [total_q] context index of each query row, ascending per request */
   const int32_t* ctx_len;      /* [num_reqs] */
   const int32_t* block_table;  /* [num_reqs][max_blocks_per_req] physical block ids */
-  const int32_t* logical_pos;  /* [num_reqs][max_blocks_per_req * block_size] pi per context token */
+  const int32_t* logical_pos;  /* [num_reqs][max_blocks_per_req * block_size] pi per context token;
+                                  16-byte aligned */
   const int32_t* span_id;      /* [num_reqs][max_blocks_per_req] */
   const uint8_t* blk_flags;    /* [num_reqs][max_blocks_per_req] MINIPIC_BLK_* bits */
 } minipic_batch;
 
 /* Launch geometry chosen for a batch (host-side planning, no GPU work). */
 typedef struct minipic_launch_info {
-  int32_t rows_per_tile;       /* query rows (token x head) per work-group */
-  int32_t tokens_per_tile;     /* query tokens per work-group */
-  int32_t num_q_tiles;         /* q tiles per request (upper bound) */
-  int32_t num_splits;          /* key-range splits per q tile (1 = no split-KV) */
-  int32_t split_blocks;        /* key blocks per split */
-  int32_t threads;             /* threads per work-group */
-  int64_t num_workgroups;      /* grid size of the attention kernel */
+  int32_t rows_per_tile;       /* query rows (token x head) per work item */
+  int32_t tokens_per_tile;     /* query tokens per q tile */
+  int32_t num_q_tiles;         /* q tiles per request (upper bound from max_q_len) */
+  int32_t num_splits;          /* most pieces one tile's key-block list may be cut into */
+  int32_t split_blocks;        /* shortest piece, in key blocks (longer pieces are chosen on the GPU) */
+  int32_t threads;             /* threads per attention work-group */
+  int64_t num_workgroups;      /* persistent attention work-groups on the current device (0: no device) */
+  int64_t num_tiles;           /* num_reqs * num_q_tiles */
+  int32_t partial_slots;       /* partial-result slots in the workspace (pieces of split tiles) */
+  int32_t reserved;
 } minipic_launch_info;
 
 const char* minipic_version(void);

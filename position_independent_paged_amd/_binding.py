@@ -53,7 +53,8 @@ class minipic_launch_info(ctypes.Structure):
     _fields_ = [
         ("rows_per_tile", ctypes.c_int32), ("tokens_per_tile", ctypes.c_int32), ("num_q_tiles", ctypes.c_int32),
         ("num_splits", ctypes.c_int32), ("split_blocks", ctypes.c_int32), ("threads", ctypes.c_int32),
-        ("num_workgroups", ctypes.c_int64),
+        ("num_workgroups", ctypes.c_int64), ("num_tiles", ctypes.c_int64), ("partial_slots", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 

@@ -1,5 +1,4 @@
-// Kernels around the flash loop: the KV-cache write, the cos/sin table and
-// the split-KV combine.
+// Kernels around the flash loop: the KV-cache write and the cos/sin table.
 #include "common.h"
 
 namespace minipic {
@@ -119,67 +118,6 @@ hipError_t launch_rope_table(float* cs, int max_pos, int d, double base, hipStre
   const int64_t n = (int64_t)max_pos * (d / 2);
   hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, cs, max_pos, d,
                      base);
-  return hipGetLastError();
-}
-
-// ---------------------------------------------------------------------------
-// Split-KV combine: merge the partial (O, m, l) of the key splits of every
-// q tile that was split, with weights 2^(m_s - max_s m_s) (log2 units).
-// ---------------------------------------------------------------------------
-template <typename T, int D>
-__global__ void __launch_bounds__(256) combine_kernel(AttnParams P, int bq, int G) {
-  const int64_t bid = blockIdx.x;
-  const int g = (int)(bid % P.hkv);
-  const int64_t rest = bid / P.hkv;
-  const int qt = (int)(rest % P.num_q_tiles);
-  const int r = (int)(rest / P.num_q_tiles);
-  const int qb = P.q_indptr[r], qe = P.q_indptr[r + 1];
-  const int row0 = qb + qt * bq;
-  if (row0 >= qe) return;
-  const int ns = P.tile_nsplit[((int64_t)r * P.num_q_tiles + qt) * P.hkv + g];
-  if (ns <= 1) return;
-  const int nq = min(bq, qe - row0);
-  const int units = nq * G * (D / 4);
-  for (int u = threadIdx.x; u < units; u += 256) {
-    const int d4 = u % (D / 4);
-    const int rg = u / (D / 4);
-    const int tok = rg / G;
-    const int head = g * G + rg % G;
-    const int64_t qrow = row0 + tok;
-    float mstar = -INFINITY;
-    for (int s = 0; s < ns; ++s) mstar = fmaxf(mstar, P.part_ml[((int64_t)s * P.total_q + qrow) * P.hq + head].x);
-    float den = 0.f;
-    f32x4 num = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < ns; ++s) {
-      const int64_t pr = ((int64_t)s * P.total_q + qrow) * P.hq + head;
-      const float2 ml = P.part_ml[pr];
-      if (ml.x == -INFINITY) continue;
-      const float wgt = exp2f(ml.x - mstar);
-      den += wgt * ml.y;
-      const f32x4 po = *(const f32x4*)(P.part_o + pr * D + 4 * d4);
-      num += wgt * po;
-    }
-    const float inv = 1.f / den;
-    T* op = (T*)P.out + (qrow * P.hq + head) * D + 4 * d4;
-    if constexpr (sizeof(T) == 4) {
-      *(f32x4*)op = num * inv;
-    } else {
-      u32x2 pk;
-      pk[0] = pack_bf16x2(num[0] * inv, num[1] * inv);
-      pk[1] = pack_bf16x2(num[2] * inv, num[3] * inv);
-      *(u32x2*)op = pk;
-    }
-  }
-}
-
-hipError_t launch_combine(const AttnParams& p, int D, int dtype, int bq, int G, int64_t grid, hipStream_t s) {
-  if (dtype == MINIPIC_BF16) {
-    if (D == 128) hipLaunchKernelGGL((combine_kernel<uint16_t, 128>), dim3((unsigned)grid), dim3(256), 0, s, p, bq, G);
-    else hipLaunchKernelGGL((combine_kernel<uint16_t, 64>), dim3((unsigned)grid), dim3(256), 0, s, p, bq, G);
-  } else {
-    if (D == 128) hipLaunchKernelGGL((combine_kernel<float, 128>), dim3((unsigned)grid), dim3(256), 0, s, p, bq, G);
-    else hipLaunchKernelGGL((combine_kernel<float, 64>), dim3((unsigned)grid), dim3(256), 0, s, p, bq, G);
-  }
   return hipGetLastError();
 }
 

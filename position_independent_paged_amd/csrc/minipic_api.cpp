@@ -13,9 +13,11 @@
 #include "common.h"
 
 namespace minipic {
-hipError_t launch_attn_bf16(const AttnParams& p, int D, int G, bool rope, int64_t grid, hipStream_t s);
-hipError_t launch_attn_f32(const AttnParams& p, int D, int G, bool rope, int64_t grid, hipStream_t s);
-hipError_t launch_combine(const AttnParams& p, int D, int dtype, int bq, int G, int64_t grid, hipStream_t s);
+hipError_t launch_plan(const PlanParams& p, int bq, hipStream_t s);
+hipError_t launch_attn_bf16(const AttnParams& p, int D, int G, bool rope, int grid, hipStream_t s);
+hipError_t launch_attn_f32(const AttnParams& p, int D, int G, bool rope, int grid, hipStream_t s);
+int attn_bf16_blocks_per_cu(int D, int G, bool rope);
+int attn_f32_blocks_per_cu(int D, int G, bool rope);
 hipError_t launch_write_kv(const void* k, const void* v, const int64_t* slots, int64_t n, int hkv, int D,
                            void* kc, void* vc, int64_t num_blocks, int dtype, hipStream_t s);
 hipError_t launch_rope_table(float* cs, int max_pos, int d, double base, hipStream_t s);
@@ -44,13 +46,15 @@ int hip_fail(hipError_t e, const char* what) {
 bool supported_dim(int d) { return d == 64 || d == 128; }
 bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
 
+// Host-side plan: sizes from host scalars only.
 struct Plan {
-  int rows, bq, nqt, splits, split_blocks, threads;
-  int64_t grid;
-  size_t off_nsplit, off_ml, off_o, bytes;
+  int rows, bq, nqt, threads, min_chunk, slots;
+  int64_t tiles, max_items;
+  size_t off_tiles, off_toks, off_blist, off_items, off_arrive, off_ml, off_o, bytes;
 };
 
 constexpr size_t kAlign = 256;
+constexpr int kSlotCap = 512;   // partial-result slots: about two pieces per CU of a 256-CU GPU
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int check_batch(const minipic_batch* b, int dtype) {
@@ -79,6 +83,7 @@ int check_batch(const minipic_batch* b, int dtype) {
       return fail(MINIPIC_ERR_INVALID_ARG, "a batch array pointer is NULL");
   }
   if (b->total_q > (int64_t)INT32_MAX) return fail(MINIPIC_ERR_INVALID_ARG, "total_q too large");
+  if ((uintptr_t)b->logical_pos % 16) return fail(MINIPIC_ERR_INVALID_ARG, "logical_pos must be 16-byte aligned");
   return MINIPIC_OK;
 }
 
@@ -99,37 +104,55 @@ void make_plan(const minipic_batch* b, int dtype, Plan* p) {
   }
   p->bq = p->rows / G;
   p->nqt = b->max_q_len > 0 ? (b->max_q_len + p->bq - 1) / p->bq : 0;
-  const int nb_max = (b->max_ctx_len + kBlock - 1) / kBlock;
-  // Key splits: a q tile whose visible blocks exceed `split_blocks` is cut into
-  // up to `splits` pieces (long PDep rows next to short span rows).
-  int splits = env_int("MINIPIC_SPLITS", 8);
-  int min_chunk = env_int("MINIPIC_MIN_SPLIT_BLOCKS", 16);
-  if (splits < 1) splits = 1;
-  if (splits > 64) splits = 64;
-  if (min_chunk < 1) min_chunk = 1;
-  int chunk = nb_max > 0 ? (nb_max + splits - 1) / splits : 1;
-  if (chunk < min_chunk) chunk = min_chunk;
-  if (nb_max <= chunk) {
-    splits = 1;
-    chunk = nb_max > 0 ? nb_max : 1;
-  } else {
-    splits = (nb_max + chunk - 1) / chunk;
-  }
-  p->splits = splits;
-  p->split_blocks = chunk;
-  p->grid = (int64_t)b->num_reqs * p->nqt * b->num_kv_heads * splits;
-  size_t off = kAlign;  // error word
-  p->off_nsplit = off;
-  off = align_up(off + sizeof(int32_t) * (size_t)b->num_reqs * p->nqt * b->num_kv_heads);
+  p->tiles = (int64_t)b->num_reqs * p->nqt;
+  p->min_chunk = env_int("MINIPIC_MIN_CHUNK", 16);
+  if (p->min_chunk < 1) p->min_chunk = 1;
+  const int64_t hkv = b->num_kv_heads;
+  int64_t slots = p->tiles * hkv * kMaxSplits;
+  if (slots > kSlotCap) slots = kSlotCap;
+  p->slots = (int)slots;
+  p->max_items = p->tiles * hkv + p->slots;
+  size_t off = kAlign;  // WsHeader
+  p->off_tiles = off;
+  off = align_up(off + sizeof(TileDesc) * (size_t)p->tiles);
+  p->off_toks = off;
+  off = align_up(off + sizeof(TokDesc) * (size_t)p->tiles * p->bq);
+  p->off_blist = off;
+  off = align_up(off + sizeof(BlkDesc) * (size_t)p->tiles * b->max_blocks_per_req);
+  p->off_items = off;
+  off = align_up(off + sizeof(Item) * (size_t)p->max_items);
+  p->off_arrive = off;
+  off = align_up(off + sizeof(uint32_t) * (size_t)p->tiles * hkv);
   p->off_ml = off;
-  if (splits > 1) {
-    off = align_up(off + sizeof(float) * 2 * (size_t)splits * b->total_q * b->num_q_heads);
-    p->off_o = off;
-    off = align_up(off + sizeof(float) * (size_t)splits * b->total_q * b->num_q_heads * b->head_dim);
-  } else {
-    p->off_o = off;
-  }
+  off = align_up(off + sizeof(float) * 2 * (size_t)p->slots * p->rows);
+  p->off_o = off;
+  off = align_up(off + sizeof(float) * (size_t)p->slots * p->rows * b->head_dim);
   p->bytes = off;
+}
+
+// Persistent grid of the attention kernel on the current device: CUs times
+// resident work-groups per CU, cached per (device, kernel configuration).
+int persistent_grid(int dtype, int D, int G, bool rope, int* grid) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  static thread_local int cache[64][2][2][4][2];
+  const int di = dtype == MINIPIC_BF16 ? 1 : 0;
+  const int Di = D == 128 ? 1 : 0;
+  const int Gi = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : 3;
+  int* c = dev < 64 ? &cache[dev][di][Di][Gi][rope ? 1 : 0] : nullptr;
+  if (c && *c > 0) {
+    *grid = *c;
+    return 0;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return -1;
+  const int per_cu = dtype == MINIPIC_BF16 ? attn_bf16_blocks_per_cu(D, G, rope) : attn_f32_blocks_per_cu(D, G, rope);
+  int g = cus * per_cu;
+  const int over = env_int("MINIPIC_GRID", 0);
+  if (over > 0) g = over;
+  if (c) *c = g;
+  *grid = g;
+  return 0;
 }
 
 int run_attention(const void* q, const void* k_cache, const void* v_cache, int64_t num_blocks,
@@ -157,7 +180,40 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, int64
   if ((uintptr_t)workspace % kAlign) return fail(MINIPIC_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
   if (workspace_bytes < pl.bytes)
     return fail(MINIPIC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, pl.bytes);
-  if (pl.grid > (int64_t)INT32_MAX) return fail(MINIPIC_ERR_INVALID_ARG, "batch too large for one launch");
+  if (pl.tiles > (int64_t)INT32_MAX / 2 || pl.max_items > (int64_t)INT32_MAX / 2)
+    return fail(MINIPIC_ERR_INVALID_ARG, "batch too large for one launch");
+  const int G = b->num_q_heads / b->num_kv_heads;
+  int grid = 0;
+  if (persistent_grid(dtype, b->head_dim, G, rope, &grid) != 0)
+    return fail(MINIPIC_ERR_HIP, "cannot query the current device");
+
+  char* ws = (char*)workspace;
+  PlanParams Q{};
+  Q.q_indptr = b->q_indptr;
+  Q.q_ctx_idx = b->q_ctx_idx;
+  Q.ctx_len = b->ctx_len;
+  Q.block_table = b->block_table;
+  Q.span_id = b->span_id;
+  Q.blk_flags = b->blk_flags;
+  Q.hdr = (WsHeader*)ws;
+  Q.tiles = (TileDesc*)(ws + pl.off_tiles);
+  Q.toks = (TokDesc*)(ws + pl.off_toks);
+  Q.blist = (BlkDesc*)(ws + pl.off_blist);
+  Q.items = (Item*)(ws + pl.off_items);
+  Q.arrive = (uint32_t*)(ws + pl.off_arrive);
+  Q.num_blocks = num_blocks;
+  Q.num_reqs = b->num_reqs;
+  Q.nqt = pl.nqt;
+  Q.num_tiles = (int)pl.tiles;
+  Q.bq = pl.bq;
+  Q.hkv = b->num_kv_heads;
+  Q.max_blocks = b->max_blocks_per_req;
+  Q.num_wg = grid;
+  Q.max_slots = pl.slots;
+  Q.max_items = (int)pl.max_items;
+  Q.min_chunk = pl.min_chunk;
+  Q.logical_pos = b->logical_pos;
+  Q.max_pos = need_table ? max_pos : 1;
 
   AttnParams P{};
   P.q = q;
@@ -165,41 +221,28 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, int64
   P.v_cache = v_cache;
   P.out = out;
   P.cos_sin = cos_sin;
-  P.q_indptr = b->q_indptr;
-  P.q_ctx_idx = b->q_ctx_idx;
-  P.ctx_len = b->ctx_len;
-  P.block_table = b->block_table;
   P.logical_pos = b->logical_pos;
-  P.span_id = b->span_id;
-  P.blk_flags = b->blk_flags;
-  char* ws = (char*)workspace;
-  P.err = (uint32_t*)ws;
-  P.tile_nsplit = (int32_t*)(ws + pl.off_nsplit);
+  P.hdr = Q.hdr;
+  P.tiles = Q.tiles;
+  P.toks = Q.toks;
+  P.blist = Q.blist;
+  P.items = Q.items;
+  P.arrive = Q.arrive;
   P.part_ml = (float2*)(ws + pl.off_ml);
   P.part_o = (float*)(ws + pl.off_o);
-  P.num_blocks = num_blocks;
-  P.total_q = b->total_q;
-  P.num_reqs = b->num_reqs;
   P.hq = b->num_q_heads;
   P.hkv = b->num_kv_heads;
   P.max_blocks = b->max_blocks_per_req;
   P.max_pos = need_table ? max_pos : 1;
-  P.num_q_tiles = pl.nqt;
-  P.num_splits = pl.splits;
-  P.split_blocks = pl.split_blocks;
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)b->head_dim);
   P.scale_log2 = scale * 1.4426950408889634f;
   P.flags = flags;
-  const int G = b->num_q_heads / b->num_kv_heads;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = dtype == MINIPIC_BF16 ? launch_attn_bf16(P, b->head_dim, G, rope, pl.grid, s)
-                                       : launch_attn_f32(P, b->head_dim, G, rope, pl.grid, s);
+  hipError_t e = launch_plan(Q, pl.bq, s);
+  if (e != hipSuccess) return hip_fail(e, "plan launch");
+  e = dtype == MINIPIC_BF16 ? launch_attn_bf16(P, b->head_dim, G, rope, grid, s)
+                            : launch_attn_f32(P, b->head_dim, G, rope, grid, s);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
-  if (pl.splits > 1) {
-    const int64_t cgrid = (int64_t)b->num_reqs * pl.nqt * b->num_kv_heads;
-    e = launch_combine(P, b->head_dim, dtype, pl.bq, G, cgrid, s);
-    if (e != hipSuccess) return hip_fail(e, "combine launch");
-  }
   return MINIPIC_OK;
 }
 
@@ -269,10 +312,17 @@ int minipic_get_launch_info(const minipic_batch* batch, int32_t dtype, minipic_l
   info->rows_per_tile = pl.rows;
   info->tokens_per_tile = pl.bq;
   info->num_q_tiles = pl.nqt;
-  info->num_splits = pl.splits;
-  info->split_blocks = pl.split_blocks;
+  info->num_splits = kMaxSplits;
+  info->split_blocks = pl.min_chunk;
   info->threads = pl.threads;
-  info->num_workgroups = pl.grid;
+  int grid = 0, ndev = 0;
+  info->num_workgroups = 0;
+  if (hipGetDeviceCount(&ndev) == hipSuccess && ndev > 0 &&
+      persistent_grid(dtype, batch->head_dim, batch->num_q_heads / batch->num_kv_heads, true, &grid) == 0)
+    info->num_workgroups = grid;
+  info->num_tiles = pl.tiles;
+  info->partial_slots = pl.slots;
+  info->reserved = 0;
   return MINIPIC_OK;
 }
 

@@ -1,0 +1,322 @@
+// Planning kernels of the position-free paged attention (gfx950).
+//
+// plan_tiles: one work-group per (request, q tile). It records every query
+// token of the tile (context index, span id, PDEP bit) and compacts the key
+// blocks at least one of its rows may see, following the block visibility of
+// "MiniPIC: Flexible Position-Independent Caching in <100LOC", §3.1.1 and
+// §3.3.1 (rule restated in common.h), into a per-tile list.
+//
+// plan_items: one work-group. It picks the piece length from the total work
+// and the number of persistent attention work-groups, cuts long tile lists
+// into pieces, assigns partial-result slots, and writes the work items
+// (tile, KV head, piece) bucketed by length, longest first. It also zeroes
+// the scheduler counter and the per-(tile, head) arrival counters, so the
+// attention kernel needs no host-side memset.
+#include <climits>
+
+#include "common.h"
+
+namespace minipic {
+
+// Descriptor of one listed key block. `lpos` is the request's row of logical
+// positions, `L` its context length. pos0 is set when the block's positions
+// (those of its tokens below L) run pos0, pos0+1, ... and the whole run
+// pos0 .. pos0+15 lies inside the cos/sin table.
+__device__ __forceinline__ BlkDesc make_blk(const PlanParams& P, const int32_t* btab, const int32_t* lpos, int L,
+                                            int kb, int span, int flags) {
+  int ph = btab[kb];
+  if (ph < 0 || (int64_t)ph >= P.num_blocks) {
+    atomicOr(&P.hdr->err, (uint32_t)MINIPIC_EW_BLOCK);
+    ph = -1;  // read as zeros by the attention kernels
+  }
+  const int4* pp = (const int4*)(lpos + (int64_t)kb * kBlock);
+  int p[kBlock];
+#pragma unroll
+  for (int i = 0; i < kBlock / 4; ++i) {
+    const int4 v = pp[i];
+    p[4 * i] = v.x;
+    p[4 * i + 1] = v.y;
+    p[4 * i + 2] = v.z;
+    p[4 * i + 3] = v.w;
+  }
+  const int nvalid = min(kBlock, L - kb * kBlock);
+  bool cons = p[0] >= 0 && p[0] <= P.max_pos - kBlock;
+#pragma unroll
+  for (int k = 1; k < kBlock; ++k) cons = cons && (k >= nvalid || p[k] == p[0] + k);
+  return BlkDesc{kb, ph, span, flags, cons ? p[0] : -1, 0, 0, 0};
+}
+
+template <int BQ>
+__global__ void __launch_bounds__(kPlanThreads) plan_tiles_kernel(PlanParams P) {
+  constexpr int NT = kPlanThreads;
+  static_assert(BQ <= NT, "one query token per thread");
+  __shared__ int qblk[BQ];
+  __shared__ int e_bq[BQ], e_span[BQ], e_pdep[BQ];
+  __shared__ int tmp[NT / 64];
+  __shared__ int s_hi, s_lo, s_anyp, s_phi;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int t = blockIdx.x;
+  const int r = t / P.nqt;
+  const int qt = t % P.nqt;
+  TileDesc* td = P.tiles + t;
+  const int qb = P.q_indptr[r];
+  const int qe = P.q_indptr[r + 1];
+  const int row0 = qb + qt * BQ;
+  if (row0 >= qe) {
+    if (tid == 0) *td = TileDesc{r, row0, 0, 0, 0, -1, 0, 0};
+    return;
+  }
+  const int nq = min(BQ, qe - row0);
+  int L = P.ctx_len[r];
+  const int Lmax = P.max_blocks * kBlock;
+  if (L > Lmax || L < 0) {
+    if (tid == 0) atomicOr(&P.hdr->err, (uint32_t)MINIPIC_EW_CTX);
+    L = L < 0 ? 0 : Lmax;
+  }
+  const int32_t* span = P.span_id + (int64_t)r * P.max_blocks;
+  const uint8_t* flg = P.blk_flags + (int64_t)r * P.max_blocks;
+  const int32_t* btab = P.block_table + (int64_t)r * P.max_blocks;
+  const int32_t* lpos = P.logical_pos + (int64_t)r * P.max_blocks * kBlock;
+
+  // ---- query tokens
+  bool valid = tid < nq;
+  int c = -1;
+  if (valid) {
+    c = P.q_ctx_idx[row0 + tid];
+    if (c < 0 || c >= L) {
+      atomicOr(&P.hdr->err, (uint32_t)MINIPIC_EW_QCTX);
+      c = c < 0 ? 0 : L - 1;
+      if (c < 0) valid = false;  // empty context: the row has nothing to attend
+    }
+  }
+  const int bq = valid ? (c >> 4) : -1;
+  int sp = 0, pd = 0;
+  if (valid) {
+    sp = span[bq];
+    pd = (flg[bq] & MINIPIC_BLK_PDEP) ? 1 : 0;
+  }
+  if (tid < BQ) {
+    P.toks[(int64_t)t * BQ + tid] = TokDesc{valid ? c : -1, sp, pd, 0};
+    qblk[tid] = bq;
+  }
+  __syncthreads();
+
+  // ---- distinct query blocks ("entries")
+  const bool first = valid && (tid == 0 || qblk[tid - 1] != bq);
+  int n_e;
+  const int idx = block_excl_scan_pred<NT>(first, tmp, &n_e);
+  if (first) {
+    e_bq[idx] = bq;
+    e_span[idx] = sp;
+    e_pdep[idx] = pd;
+  }
+  __syncthreads();
+
+  // ---- key range (wave 0)
+  if (tid < 64) {
+    int hi = -1, mn = INT_MAX, anyp = 0, phi = -1;
+    for (int e = lane; e < n_e; e += 64) {
+      const int b = e_bq[e];
+      hi = max(hi, b);
+      mn = min(mn, b);
+      if (e_pdep[e]) {
+        anyp = 1;
+        phi = max(phi, b);
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      hi = max(hi, __shfl_xor(hi, o, 64));
+      mn = min(mn, __shfl_xor(mn, o, 64));
+      anyp |= __shfl_xor(anyp, o, 64);
+      phi = max(phi, __shfl_xor(phi, o, 64));
+    }
+    // start of the run of equal span ids that holds the smallest query block
+    int lo = 0;
+    if (!anyp && mn != INT_MAX) {
+      const int s0 = span[mn];
+      int base = mn;
+      while (true) {
+        const int b = base - 1 - lane;
+        const bool stop = (b < 0) || (span[b] != s0);
+        const uint64_t m = __ballot(stop);
+        if (m) {
+          lo = base - (__ffsll((unsigned long long)m) - 1);
+          break;
+        }
+        base -= 64;
+      }
+    }
+    if (lane == 0) {
+      s_hi = hi;
+      s_lo = lo;
+      s_anyp = anyp;
+      s_phi = phi;
+    }
+  }
+  __syncthreads();
+  const int lo = s_lo, hi = s_hi, anyp = s_anyp, phi = s_phi;
+
+  // ---- compacted list: GLOBAL blocks below lo (visible to every row), then
+  // the blocks of [lo, hi] some row sees
+  BlkDesc* out = P.blist + (int64_t)t * P.max_blocks;
+  int n = 0;
+  for (int base = 0; base < lo; base += NT) {
+    const int kb = base + tid;
+    int f = 0;
+    if (kb < lo) f = flg[kb];
+    const bool is = (f & MINIPIC_BLK_GLOBAL) != 0;
+    int tot;
+    const int i = block_excl_scan_pred<NT>(is, tmp, &tot);
+    if (is) out[n + i] = make_blk(P, btab, lpos, L, kb, span[kb], f);
+    n += tot;
+  }
+  for (int base = lo; base <= hi; base += NT) {
+    const int kb = base + tid;
+    bool vis = false;
+    int f = 0, s = 0;
+    if (kb <= hi) {
+      f = flg[kb];
+      s = span[kb];
+      if (anyp && kb <= phi) {
+        vis = true;
+      } else {
+        for (int e = 0; e < n_e; ++e) {
+          if (kb <= e_bq[e] && (e_pdep[e] || (f & MINIPIC_BLK_GLOBAL) || e_span[e] == s)) {
+            vis = true;
+            break;
+          }
+        }
+      }
+    }
+    int tot;
+    const int i = block_excl_scan_pred<NT>(vis, tmp, &tot);
+    if (vis) out[n + i] = make_blk(P, btab, lpos, L, kb, s, f);
+    n += tot;
+  }
+  if (tid == 0) *td = TileDesc{r, row0, nq, n, 0, -1, 0, 0};
+}
+
+// ---------------------------------------------------------------------------
+
+template <int NT>
+__device__ long long block_sum_ll(long long v, unsigned long long* red) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  if (lane == 0) red[w] = (unsigned long long)v;
+  __syncthreads();
+  long long s = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) s += (long long)red[i];
+  __syncthreads();
+  return s;
+}
+
+__device__ __forceinline__ int num_pieces(int n, int chunk) {
+  if (n <= 0) return 0;
+  const int ns = (n + chunk - 1) / chunk;
+  return ns < kMaxSplits ? ns : kMaxSplits;
+}
+
+__device__ __forceinline__ int piece_start(int n, int ns, int s) { return (int)(((int64_t)s * n) / ns); }
+
+__global__ void __launch_bounds__(kItemThreads) plan_items_kernel(PlanParams P) {
+  constexpr int NT = kItemThreads;
+  static_assert(kCostBins == NT, "one cost bucket per thread");
+  __shared__ unsigned long long red[NT / 64];
+  __shared__ int tmp[NT / 64];
+  __shared__ int bins[kCostBins];
+  const int tid = threadIdx.x;
+  const int T = P.num_tiles;
+  const int H = P.hkv;
+
+  // ---- piece length: about two pieces of work per persistent work-group,
+  // never shorter than min_chunk, and few enough split tiles to fit the
+  // partial-result slots
+  long long work = 0;
+  for (int t = tid; t < T; t += NT) work += P.tiles[t].nlist;
+  work = block_sum_ll<NT>(work, red) * H;
+  const long long per = 2LL * P.num_wg;
+  long long cl = (work + per - 1) / per;
+  int chunk = (int)(cl < (long long)P.min_chunk ? P.min_chunk : (cl > (1LL << 30) ? (1LL << 30) : cl));
+  for (int iter = 0; iter < 40; ++iter) {
+    long long slots = 0;
+    for (int t = tid; t < T; t += NT) {
+      const int ns = num_pieces(P.tiles[t].nlist, chunk);
+      if (ns > 1) slots += (long long)ns * H;
+    }
+    slots = block_sum_ll<NT>(slots, red);
+    if (slots <= P.max_slots || chunk >= (1 << 30)) break;
+    chunk *= 2;
+  }
+
+  // ---- pieces and slots per tile
+  int slot_base = 0;
+  for (int t0 = 0; t0 < T; t0 += NT) {
+    const int t = t0 + tid;
+    const int ns = t < T ? num_pieces(P.tiles[t].nlist, chunk) : 0;
+    int tot;
+    const int off = block_excl_scan<NT>(ns > 1 ? ns * H : 0, tmp, &tot);
+    if (t < T) {
+      P.tiles[t].nsplit = ns;
+      P.tiles[t].slot0 = ns > 1 ? slot_base + off : -1;
+    }
+    slot_base += tot;
+  }
+
+  // ---- bucket the items by length (key blocks), longest first
+  bins[tid] = 0;
+  __syncthreads();
+  for (int t = tid; t < T; t += NT) {
+    const int n = P.tiles[t].nlist;
+    const int ns = num_pieces(n, chunk);
+    for (int s = 0; s < ns; ++s) {
+      const int cost = piece_start(n, ns, s + 1) - piece_start(n, ns, s);
+      atomicAdd(&bins[min(cost, kCostBins - 1)], H);
+    }
+  }
+  __syncthreads();
+  const int b = kCostBins - 1 - tid;  // thread tid owns bucket b (descending order)
+  int total;
+  const int start = block_excl_scan<NT>(bins[b], tmp, &total);
+  bins[b] = start;
+  __syncthreads();
+  for (int t = tid; t < T; t += NT) {
+    const int n = P.tiles[t].nlist;
+    const int ns = num_pieces(n, chunk);
+    for (int s = 0; s < ns; ++s) {
+      const int p0 = piece_start(n, ns, s);
+      const int p1 = piece_start(n, ns, s + 1);
+      const int pos = atomicAdd(&bins[min(p1 - p0, kCostBins - 1)], H);
+      for (int g = 0; g < H; ++g) P.items[pos + g] = Item{t, p0, p1, pack_gsn(g, s, ns)};
+    }
+  }
+  for (int i = tid; i < T * H; i += NT) P.arrive[i] = 0u;
+  if (tid == 0) {
+    P.hdr->next_item = 0u;
+    P.hdr->num_items = (uint32_t)total;
+    P.hdr->chunk = (uint32_t)chunk;
+  }
+}
+
+hipError_t launch_plan(const PlanParams& p, int bq, hipStream_t s) {
+  switch (bq) {
+    case 32: hipLaunchKernelGGL(plan_tiles_kernel<32>, dim3(p.num_tiles), dim3(kPlanThreads), 0, s, p); break;
+    case 64: hipLaunchKernelGGL(plan_tiles_kernel<64>, dim3(p.num_tiles), dim3(kPlanThreads), 0, s, p); break;
+    case 128: hipLaunchKernelGGL(plan_tiles_kernel<128>, dim3(p.num_tiles), dim3(kPlanThreads), 0, s, p); break;
+    case 256: hipLaunchKernelGGL(plan_tiles_kernel<256>, dim3(p.num_tiles), dim3(kPlanThreads), 0, s, p); break;
+    case 8: hipLaunchKernelGGL(plan_tiles_kernel<8>, dim3(p.num_tiles), dim3(kPlanThreads), 0, s, p); break;
+    case 16: hipLaunchKernelGGL(plan_tiles_kernel<16>, dim3(p.num_tiles), dim3(kPlanThreads), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(plan_items_kernel, dim3(1), dim3(kItemThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace minipic

@@ -44,8 +44,8 @@ def test_version_and_status_strings():
 
 def _batch(**kw):
     d = dict(num_reqs=1, num_q_heads=32, num_kv_heads=8, head_dim=128, block_size=16, max_blocks_per_req=10,
-             total_q=100, max_q_len=100, max_ctx_len=160, q_indptr=8, q_ctx_idx=8, ctx_len=8, block_table=8,
-             logical_pos=8, span_id=8, blk_flags=8)
+             total_q=100, max_q_len=100, max_ctx_len=160, q_indptr=256, q_ctx_idx=256, ctx_len=256, block_table=256,
+             logical_pos=256, span_id=256, blk_flags=256)
     d.update(kw)
     return minipic_batch(**d)
 
@@ -67,6 +67,7 @@ def _attn(b, dtype=1, ws_bytes=1 << 30, q=256, out=256, ws=256, table=256, max_p
     (dict(total_q=-5), -1),
     (dict(q_indptr=None), -1),
     (dict(max_q_len=0), -1),
+    (dict(logical_pos=256 + 4), -1),                 # not 16-byte aligned
 ])
 def test_attention_rejects_bad_batch(kw, code):
     assert _attn(_batch(**kw)) == code
@@ -119,15 +120,18 @@ def test_launch_plan_and_workspace():
     b = _batch(total_q=15872, max_q_len=15872, max_ctx_len=31232, max_blocks_per_req=1952)
     info = pip.minipic_get_launch_info(b, 1)
     assert info["tokens_per_tile"] == 64 and info["rows_per_tile"] == 256
-    assert info["num_q_tiles"] == 248
-    assert info["num_splits"] * info["split_blocks"] >= 1952
+    assert info["num_q_tiles"] == 248 and info["num_tiles"] == 248
+    assert info["threads"] == 512
     ws = pip.minipic_workspace_size(b, 1)
-    S = info["num_splits"]
-    assert ws >= S * 15872 * 32 * (128 + 2) * 4
-    # short contexts are not split
+    # per-tile key-block lists (16 B per block) and the partial-result slots (fp32 O, m, l per row)
+    assert ws >= 248 * 1952 * 16 + info["partial_slots"] * 256 * (128 + 2) * 4
+    assert info["partial_slots"] >= 64          # room to split every (tile, head) of the long suffix
+    # a tiny batch gets a small workspace
     small = _batch(total_q=80, max_q_len=80, max_ctx_len=80, max_blocks_per_req=5, num_q_heads=4,
                    num_kv_heads=2, head_dim=64)
-    assert pip.minipic_get_launch_info(small, 0)["num_splits"] == 1
+    si = pip.minipic_get_launch_info(small, 0)
+    assert si["tokens_per_tile"] == 32 and si["num_q_tiles"] == 3
+    assert pip.minipic_workspace_size(small, 0) < 8 << 20
 
 
 @pytest.mark.parametrize("name", ["c1", "c1_cached", "c3_small", "c4_small", "c5_small", "c2"])
