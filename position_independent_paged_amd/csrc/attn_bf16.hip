@@ -32,9 +32,7 @@
 //     accumulators are rescaled only when a row max grows by more than 2^8,
 //     which is exact (numerator and denominator share the stale max).
 //   * A tile whose list was cut into pieces: every piece stores (O, m, l) in
-//     fp32 to its slot; the piece that arrives last reads all of them back and
-//     merges them in piece order (weights 2^(m_s - max m)), so the result does
-//     not depend on which piece finished last.
+//     fp32 to its slot; merge_kernel combines them afterwards.
 #include "common.h"
 
 namespace minipic {
@@ -74,7 +72,7 @@ __global__ void __launch_bounds__(kNT, 1) attn_bf16_kernel(AttnParams P) {
   using L = Lds<D>;
   using St = Stage<D, ROPE>;
   __shared__ BlkDesc lst[kListMax];
-  __shared__ int s_next, s_arrived;
+  __shared__ int s_next;
   __shared__ __attribute__((aligned(16))) __bf16 kl[2 * L::KSZ];
   __shared__ __attribute__((aligned(16))) __bf16 vl[2 * L::VSZ];
 
@@ -90,11 +88,9 @@ __global__ void __launch_bounds__(kNT, 1) attn_bf16_kernel(AttnParams P) {
   const __bf16* kc = (const __bf16*)P.k_cache;
   const __bf16* vc = (const __bf16*)P.v_cache;
   const float sl2 = P.scale_log2;
-  const int n_items = (int)P.hdr->num_items;
-
   int it = next_item(P.hdr, &s_next);
-  while (it < n_items) {
-    if (tid == 0) s_next = (int)atomicAdd(&P.hdr->next_item, 1u);  // the following item
+  while (it >= 0) {
+    if (tid == 0) s_next = claim_item(P.hdr);  // the following item
     const Item item = P.items[it];
     const int g = item.gsn & 0xff;
     const int sp = (item.gsn >> 8) & 0xfff;
@@ -357,60 +353,18 @@ __global__ void __launch_bounds__(kNT, 1) attn_bf16_kernel(AttnParams P) {
             *(u32x2*)(op + 32 * dg + 8 * j + 4 * h) = u;
           }
       }
-    } else {
-      const int slot_g = td.slot0 + g * ns;   // slots of this tile and KV head, one per piece
-      if (rvalid) {
-        float* po = P.part_o + ((int64_t)(slot_g + sp) * kRows + row) * D;
+    } else if (rvalid) {
+      // a piece of a split tile: fp32 partial result to its slot (merged by merge_kernel)
+      const int64_t pr = (int64_t)(td.slot0 + g * ns + sp) * kRows + row;
+      float* po = P.part_o + pr * D;
 #pragma unroll
-        for (int dg = 0; dg < D / 32; ++dg)
+      for (int dg = 0; dg < D / 32; ++dg)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const f32x4 u = {o[dg][4 * j], o[dg][4 * j + 1], o[dg][4 * j + 2], o[dg][4 * j + 3]};
-            *(f32x4*)(po + 32 * dg + 8 * j + 4 * h) = u;
-          }
-        if (h == 0) P.part_ml[(int64_t)(slot_g + sp) * kRows + row] = make_float2(m_run, l_tot);
-      }
-      __threadfence();
-      __syncthreads();
-      if (tid == 0) s_arrived = (int)atomicAdd(&P.arrive[(int64_t)item.tile * P.hkv + g], 1u);
-      __syncthreads();
-      if (s_arrived == ns - 1) {
-        // last piece: merge every piece (its own included, read back) in piece order
-        __threadfence();
-        if (rvalid) {
-          float mstar = -INFINITY;
-          for (int s = 0; s < ns; ++s) mstar = fmaxf(mstar, P.part_ml[(int64_t)(slot_g + s) * kRows + row].x);
-#pragma unroll
-          for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
-          float den = 0.f;
-          for (int s = 0; s < ns; ++s) {
-            const int64_t pr = (int64_t)(slot_g + s) * kRows + row;
-            const float2 ml = P.part_ml[pr];
-            if (ml.x == -INFINITY) continue;
-            const float wgt = exp2f(ml.x - mstar);
-            den += wgt * ml.y;
-            const float* po = P.part_o + pr * D;
-#pragma unroll
-            for (int dg = 0; dg < D / 32; ++dg)
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const f32x4 u = *(const f32x4*)(po + 32 * dg + 8 * j + 4 * h);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) o[dg][4 * j + q] += wgt * u[q];
-              }
-          }
-          const float inv = 1.f / den;
-#pragma unroll
-          for (int dg = 0; dg < D / 32; ++dg)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              u32x2 u;
-              u[0] = pack_bf16x2(o[dg][4 * j] * inv, o[dg][4 * j + 1] * inv);
-              u[1] = pack_bf16x2(o[dg][4 * j + 2] * inv, o[dg][4 * j + 3] * inv);
-              *(u32x2*)(op + 32 * dg + 8 * j + 4 * h) = u;
-            }
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 u = {o[dg][4 * j], o[dg][4 * j + 1], o[dg][4 * j + 2], o[dg][4 * j + 3]};
+          *(f32x4*)(po + 32 * dg + 8 * j + 4 * h) = u;
         }
-      }
+      if (h == 0) P.part_ml[pr] = make_float2(m_run, l_tot);
     }
     __syncthreads();
     it = __builtin_amdgcn_readfirstlane(s_next);

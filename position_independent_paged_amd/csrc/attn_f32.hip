@@ -20,7 +20,7 @@ __global__ void __launch_bounds__(kNTf) attn_f32_kernel(AttnParams P) {
   constexpr int BQ = kRowsF / G;
   constexpr int DQ = D / 4;
   __shared__ BlkDesc lst[kListMaxF];
-  __shared__ int s_next, s_arrived;
+  __shared__ int s_next;
   __shared__ float kt[kBlock][D + 1];
   __shared__ float vt[kBlock][D + 1];
 
@@ -32,11 +32,9 @@ __global__ void __launch_bounds__(kNTf) attn_f32_kernel(AttnParams P) {
   const float sl2 = P.scale_log2;
   const float* kc = (const float*)P.k_cache;
   const float* vc = (const float*)P.v_cache;
-  const int n_items = (int)P.hdr->num_items;
-
   int it = next_item(P.hdr, &s_next);
-  while (it < n_items) {
-    if (tid == 0) s_next = (int)atomicAdd(&P.hdr->next_item, 1u);
+  while (it >= 0) {
+    if (tid == 0) s_next = claim_item(P.hdr);
     const Item item = P.items[it];
     const int g = item.gsn & 0xff;
     const int sp = (item.gsn >> 8) & 0xfff;
@@ -149,43 +147,13 @@ __global__ void __launch_bounds__(kNTf) attn_f32_kernel(AttnParams P) {
 #pragma unroll
         for (int i = 0; i < DQ; ++i) op[i] = o[i] * inv;
       }
-    } else {
-      const int slot_g = td.slot0 + g * ns;
-      if (rvalid) {
-        const int64_t pr = (int64_t)(slot_g + sp) * kRowsF + row;
-        float* po = P.part_o + pr * D + qd;
+    } else if (rvalid) {
+      // a piece of a split tile: fp32 partial result to its slot (merged by merge_kernel)
+      const int64_t pr = (int64_t)(td.slot0 + g * ns + sp) * kRowsF + row;
+      float* po = P.part_o + pr * D + qd;
 #pragma unroll
-        for (int i = 0; i < DQ; ++i) po[i] = o[i];
-        if ((tid & 3) == 0) P.part_ml[pr] = make_float2(m_run, l_run);
-      }
-      __threadfence();
-      __syncthreads();
-      if (tid == 0) s_arrived = (int)atomicAdd(&P.arrive[(int64_t)item.tile * P.hkv + g], 1u);
-      __syncthreads();
-      if (s_arrived == ns - 1) {
-        // last piece: merge every piece (its own included, read back) in piece order
-        __threadfence();
-        if (rvalid) {
-          float mstar = -INFINITY;
-          for (int s = 0; s < ns; ++s) mstar = fmaxf(mstar, P.part_ml[(int64_t)(slot_g + s) * kRowsF + row].x);
-#pragma unroll
-          for (int i = 0; i < DQ; ++i) o[i] = 0.f;
-          float den = 0.f;
-          for (int s = 0; s < ns; ++s) {
-            const int64_t pr = (int64_t)(slot_g + s) * kRowsF + row;
-            const float2 ml = P.part_ml[pr];
-            if (ml.x == -INFINITY) continue;
-            const float wgt = exp2f(ml.x - mstar);
-            den += wgt * ml.y;
-            const float* po = P.part_o + pr * D + qd;
-#pragma unroll
-            for (int i = 0; i < DQ; ++i) o[i] += wgt * po[i];
-          }
-          const float inv = 1.f / den;
-#pragma unroll
-          for (int i = 0; i < DQ; ++i) op[i] = o[i] * inv;
-        }
-      }
+      for (int i = 0; i < DQ; ++i) po[i] = o[i];
+      if ((tid & 3) == 0) P.part_ml[pr] = make_float2(m_run, l_run);
     }
     __syncthreads();
     it = __builtin_amdgcn_readfirstlane(s_next);

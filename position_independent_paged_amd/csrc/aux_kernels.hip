@@ -1,4 +1,5 @@
-// Kernels around the flash loop: the KV-cache write and the cos/sin table.
+// Kernels around the flash loop: the KV-cache write, the cos/sin table and
+// the merge of split tiles.
 #include "common.h"
 
 namespace minipic {
@@ -118,6 +119,66 @@ hipError_t launch_rope_table(float* cs, int max_pos, int d, double base, hipStre
   const int64_t n = (int64_t)max_pos * (d / 2);
   hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, cs, max_pos, d,
                      base);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Merge of split tiles: for every split (tile, KV head) group listed by
+// plan_items, combine the pieces' partial results (O, m, l), m in log2 units,
+// as O = sum_s 2^(m_s - m*) O_s / sum_s 2^(m_s - m*) l_s with m* = max_s m_s,
+// summing in piece order. A row is handled by D/4 threads (4 elements each).
+// ---------------------------------------------------------------------------
+template <typename T, int D, int ROWS>
+__global__ void __launch_bounds__(256) merge_kernel(AttnParams P, int G) {
+  constexpr int TPR = D / 4;             // threads per row
+  constexpr int RPP = 256 / TPR;         // rows per pass
+  const int ngroups = (int)P.hdr->num_groups;
+  const int bq = ROWS / G;
+  for (int gi = blockIdx.x; gi < ngroups; gi += gridDim.x) {
+    const Group grp = P.groups[gi];
+    const TileDesc td = P.tiles[grp.tile];
+    for (int row = threadIdx.x / TPR; row < ROWS; row += RPP) {
+      const int tok = row / G;
+      if (tok >= td.nq || P.toks[(int64_t)grp.tile * bq + tok].c < 0) continue;
+      const int d4 = threadIdx.x % TPR;
+      float mstar = -INFINITY;
+      for (int s = 0; s < grp.nsplit; ++s)
+        mstar = fmaxf(mstar, P.part_ml[(int64_t)(grp.slot0 + s) * ROWS + row].x);
+      float den = 0.f;
+      f32x4 num = {0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < grp.nsplit; ++s) {
+        const int64_t pr = (int64_t)(grp.slot0 + s) * ROWS + row;
+        const float2 ml = P.part_ml[pr];
+        if (ml.x == -INFINITY) continue;
+        const float wgt = exp2f(ml.x - mstar);
+        den += wgt * ml.y;
+        const f32x4 po = *(const f32x4*)(P.part_o + pr * D + 4 * d4);
+        num += wgt * po;
+      }
+      const float inv = 1.f / den;
+      const int64_t qrow = (int64_t)td.row0 + tok;
+      const int head = grp.g * G + row % G;
+      T* op = (T*)P.out + (qrow * P.hq + head) * D + 4 * d4;
+      if constexpr (sizeof(T) == 4) {
+        *(f32x4*)op = num * inv;
+      } else {
+        u32x2 pk;
+        pk[0] = pack_bf16x2(num[0] * inv, num[1] * inv);
+        pk[1] = pack_bf16x2(num[2] * inv, num[3] * inv);
+        *(u32x2*)op = pk;
+      }
+    }
+  }
+}
+
+hipError_t launch_merge(const AttnParams& p, int D, int dtype, int G, int grid, hipStream_t s) {
+  if (dtype == MINIPIC_BF16) {
+    if (D == 128) hipLaunchKernelGGL((merge_kernel<uint16_t, 128, 256>), dim3(grid), dim3(256), 0, s, p, G);
+    else hipLaunchKernelGGL((merge_kernel<uint16_t, 64, 256>), dim3(grid), dim3(256), 0, s, p, G);
+  } else {
+    if (D == 128) hipLaunchKernelGGL((merge_kernel<float, 128, 64>), dim3(grid), dim3(256), 0, s, p, G);
+    else hipLaunchKernelGGL((merge_kernel<float, 64, 64>), dim3(grid), dim3(256), 0, s, p, G);
+  }
   return hipGetLastError();
 }
 

@@ -9,8 +9,13 @@
 //               partial-result slots to split tiles, and writes the work items
 //               (tile, KV head, piece of the key list) sorted longest first.
 //   attention   a persistent grid (about one work-group per CU) that takes
-//               items from an atomic counter; for a split tile the piece that
-//               finishes last merges the partial results of the others.
+//               items from an atomic counter; a piece of a split tile writes
+//               its fp32 partial result (O, m, l) to its slot.
+//   merge       one work-group per split (tile, KV head): log-sum-exp merge
+//               of the pieces, in piece order. A separate launch: a fence
+//               inside the attention kernel would write back and invalidate
+//               the L2 of the XCD, evicting the K/V tiles the other
+//               work-groups there are reusing.
 //
 // The visibility rule follows "MiniPIC: Flexible Position-Independent Caching
 // in <100LOC", §3.1.1 (SSep / PDep) and §3.3.1 (documents and the system
@@ -45,12 +50,31 @@ constexpr int kCostBins = 1024;   // item sort buckets (cost in key blocks, clip
 constexpr int kPlanThreads = 256; // plan_tiles work-group size
 constexpr int kItemThreads = 1024;// plan_items work-group size
 
+// Work items are kept in kQueues queues, one per XCD of the GPU. The
+// dispatcher places work-group b on XCD b % 8, so work-group b drains queue
+// b % kQueues first; items that read the same K/V blocks share a queue, so
+// the work-groups reading them share one L2. An empty queue is left for the
+// next one (work stealing).
+constexpr int kQueues = 8;
+
 // Header of the workspace (first 256 bytes).
 struct WsHeader {
-  uint32_t err;        // MINIPIC_EW_* bits
-  uint32_t next_item;  // dynamic scheduler counter (zeroed by plan_items)
-  uint32_t num_items;  // written by plan_items
-  uint32_t chunk;      // key blocks per piece chosen by plan_items
+  uint32_t err;                 // MINIPIC_EW_* bits
+  uint32_t num_items;           // written by plan_items
+  uint32_t chunk;               // key blocks per piece chosen by plan_items
+  uint32_t num_groups;          // split (tile, KV head) groups listed for the merge
+  uint32_t next[kQueues];       // per-queue scheduler counters (zeroed by plan_items)
+  uint32_t qstart[kQueues];     // first item of each queue
+  uint32_t qcount[kQueues];     // items in each queue
+};
+static_assert(sizeof(WsHeader) <= 256, "workspace header");
+
+// One split (tile, KV head): its pieces occupy slots slot0 .. slot0+nsplit-1.
+struct Group {
+  int32_t tile;
+  int32_t g;
+  int32_t nsplit;
+  int32_t slot0;
 };
 
 // One q tile (written by plan_tiles; nsplit / slot0 completed by plan_items).
@@ -109,7 +133,7 @@ struct PlanParams {
   TokDesc* toks;       // [num_tiles][bq]
   BlkDesc* blist;      // [num_tiles][max_blocks]
   Item* items;         // [max_items]
-  uint32_t* arrive;    // [num_tiles][hkv]
+  Group* groups;       // [max_slots / 2]
   int64_t num_blocks;
   int32_t num_reqs;
   int32_t nqt;         // q tiles per request (host upper bound)
@@ -138,13 +162,14 @@ struct AttnParams {
   const TokDesc* toks;
   const BlkDesc* blist;
   const Item* items;
-  uint32_t* arrive;
+  const Group* groups;
   float2* part_ml;     // [slots][rows] (m in log2 units, l)
   float* part_o;       // [slots][rows][D]
   int32_t hq;
   int32_t hkv;
   int32_t max_blocks;
   int32_t max_pos;
+  int32_t max_groups;  // capacity of the group list
   float scale_log2;    // softmax_scale * log2(e)
   uint32_t flags;
 };
@@ -209,10 +234,25 @@ __device__ __forceinline__ bool block_visible(int kb, int span, int flags, int b
   return kb <= bq && (pdep_row || (flags & MINIPIC_BLK_GLOBAL) || span == span_row);
 }
 
-// Take the next work item: thread 0 bumps the counter, every thread reads the
-// value through LDS. Contains a barrier.
+// Claim the next work item for this work-group (thread 0 only): the own
+// queue first, then the others in turn. Returns an index into the item array,
+// or -1 when every queue is drained.
+__device__ __forceinline__ int claim_item(WsHeader* hdr) {
+  const int home = blockIdx.x % kQueues;
+  for (int k = 0; k < kQueues; ++k) {
+    const int q = (home + k) % kQueues;
+    const uint32_t cnt = hdr->qcount[q];
+    if (__hip_atomic_load(&hdr->next[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= cnt) continue;
+    const uint32_t i = atomicAdd(&hdr->next[q], 1u);
+    if (i < cnt) return (int)(hdr->qstart[q] + i);
+  }
+  return -1;
+}
+
+// Take the next work item: thread 0 claims it, every thread reads the value
+// through LDS. Contains barriers.
 __device__ __forceinline__ int next_item(WsHeader* hdr, int* slot) {
-  if (threadIdx.x == 0) *slot = (int)atomicAdd(&hdr->next_item, 1u);
+  if (threadIdx.x == 0) *slot = claim_item(hdr);
   __syncthreads();
   const int v = __builtin_amdgcn_readfirstlane(*slot);  // uniform: lets item fields live in SGPRs
   __syncthreads();

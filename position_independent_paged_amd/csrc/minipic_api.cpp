@@ -21,6 +21,7 @@ int attn_f32_blocks_per_cu(int D, int G, bool rope);
 hipError_t launch_write_kv(const void* k, const void* v, const int64_t* slots, int64_t n, int hkv, int D,
                            void* kc, void* vc, int64_t num_blocks, int dtype, hipStream_t s);
 hipError_t launch_rope_table(float* cs, int max_pos, int d, double base, hipStream_t s);
+hipError_t launch_merge(const AttnParams& p, int D, int dtype, int G, int grid, hipStream_t s);
 }  // namespace minipic
 
 using namespace minipic;
@@ -48,9 +49,9 @@ bool supported_group(int g) { return g == 1 || g == 2 || g == 4 || g == 8; }
 
 // Host-side plan: sizes from host scalars only.
 struct Plan {
-  int rows, bq, nqt, threads, min_chunk, slots;
+  int rows, bq, nqt, threads, min_chunk, slots, max_groups;
   int64_t tiles, max_items;
-  size_t off_tiles, off_toks, off_blist, off_items, off_arrive, off_ml, off_o, bytes;
+  size_t off_tiles, off_toks, off_blist, off_items, off_groups, off_ml, off_o, bytes;
 };
 
 constexpr size_t kAlign = 256;
@@ -121,8 +122,9 @@ void make_plan(const minipic_batch* b, int dtype, Plan* p) {
   off = align_up(off + sizeof(BlkDesc) * (size_t)p->tiles * b->max_blocks_per_req);
   p->off_items = off;
   off = align_up(off + sizeof(Item) * (size_t)p->max_items);
-  p->off_arrive = off;
-  off = align_up(off + sizeof(uint32_t) * (size_t)p->tiles * hkv);
+  p->max_groups = p->slots / 2 > 0 ? p->slots / 2 : 1;  // a split group holds >= 2 pieces
+  p->off_groups = off;
+  off = align_up(off + sizeof(Group) * (size_t)p->max_groups);
   p->off_ml = off;
   off = align_up(off + sizeof(float) * 2 * (size_t)p->slots * p->rows);
   p->off_o = off;
@@ -200,7 +202,7 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, int64
   Q.toks = (TokDesc*)(ws + pl.off_toks);
   Q.blist = (BlkDesc*)(ws + pl.off_blist);
   Q.items = (Item*)(ws + pl.off_items);
-  Q.arrive = (uint32_t*)(ws + pl.off_arrive);
+  Q.groups = (Group*)(ws + pl.off_groups);
   Q.num_blocks = num_blocks;
   Q.num_reqs = b->num_reqs;
   Q.nqt = pl.nqt;
@@ -227,7 +229,8 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, int64
   P.toks = Q.toks;
   P.blist = Q.blist;
   P.items = Q.items;
-  P.arrive = Q.arrive;
+  P.groups = Q.groups;
+  P.max_groups = pl.max_groups;
   P.part_ml = (float2*)(ws + pl.off_ml);
   P.part_o = (float*)(ws + pl.off_o);
   P.hq = b->num_q_heads;
@@ -243,6 +246,9 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, int64
   e = dtype == MINIPIC_BF16 ? launch_attn_bf16(P, b->head_dim, G, rope, grid, s)
                             : launch_attn_f32(P, b->head_dim, G, rope, grid, s);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
+  const int mgrid = pl.max_groups < 1024 ? pl.max_groups : 1024;
+  e = launch_merge(P, b->head_dim, dtype, G, mgrid, s);
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
   return MINIPIC_OK;
 }
 

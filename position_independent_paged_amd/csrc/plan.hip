@@ -9,9 +9,9 @@
 // plan_items: one work-group. It picks the piece length from the total work
 // and the number of persistent attention work-groups, cuts long tile lists
 // into pieces, assigns partial-result slots, and writes the work items
-// (tile, KV head, piece) bucketed by length, longest first. It also zeroes
-// the scheduler counter and the per-(tile, head) arrival counters, so the
-// attention kernel needs no host-side memset.
+// (tile, KV head, piece) into per-XCD queues, longest first, and the list of
+// split (tile, KV head) groups for the merge. It also zeroes the scheduler
+// counter, so the attention kernel needs no host-side memset.
 #include <climits>
 
 #include "common.h"
@@ -224,12 +224,30 @@ __device__ __forceinline__ int num_pieces(int n, int chunk) {
 
 __device__ __forceinline__ int piece_start(int n, int ns, int s) { return (int)(((int64_t)s * n) / ns); }
 
+// Queue of an item: items reading the same K/V blocks (same KV head, same
+// first key block) land in the same queue. With a multiple of kQueues KV
+// heads, queue = head; otherwise a hash of (request, head, first block).
+__device__ __forceinline__ int item_queue(const PlanParams& P, int t, int g, int p0) {
+  if (P.hkv % kQueues == 0) return g % kQueues;
+  const int kb = P.blist[(int64_t)t * P.max_blocks + p0].kb;
+  uint32_t h = (uint32_t)P.tiles[t].r * 0x9E3779B1u ^ (uint32_t)g * 0x85EBCA77u ^ (uint32_t)kb * 0xC2B2AE3Du;
+  h ^= h >> 15;
+  h *= 0x2C1B3C6Du;
+  h ^= h >> 12;
+  return (int)(h % kQueues);
+}
+
+// Counter of (queue, cost): queue-major, longest pieces first inside a queue.
+__device__ __forceinline__ int bin_index(int q, int cost) {
+  return q * kCostBins + (kCostBins - 1 - min(cost, kCostBins - 1));
+}
+
 __global__ void __launch_bounds__(kItemThreads) plan_items_kernel(PlanParams P) {
   constexpr int NT = kItemThreads;
-  static_assert(kCostBins == NT, "one cost bucket per thread");
+  static_assert((kQueues * kCostBins) % NT == 0, "whole counters per thread");
   __shared__ unsigned long long red[NT / 64];
   __shared__ int tmp[NT / 64];
-  __shared__ int bins[kCostBins];
+  __shared__ int bins[kQueues * kCostBins];
   const int tid = threadIdx.x;
   const int T = P.num_tiles;
   const int H = P.hkv;
@@ -268,22 +286,44 @@ __global__ void __launch_bounds__(kItemThreads) plan_items_kernel(PlanParams P) 
     slot_base += tot;
   }
 
-  // ---- bucket the items by length (key blocks), longest first
-  bins[tid] = 0;
+  // ---- bucket the items by (queue, length), longest first within a queue
+  for (int f = tid; f < kQueues * kCostBins; f += NT) bins[f] = 0;
   __syncthreads();
   for (int t = tid; t < T; t += NT) {
     const int n = P.tiles[t].nlist;
     const int ns = num_pieces(n, chunk);
     for (int s = 0; s < ns; ++s) {
-      const int cost = piece_start(n, ns, s + 1) - piece_start(n, ns, s);
-      atomicAdd(&bins[min(cost, kCostBins - 1)], H);
+      const int p0 = piece_start(n, ns, s);
+      const int cost = piece_start(n, ns, s + 1) - p0;
+      for (int g = 0; g < H; ++g)
+        atomicAdd(&bins[bin_index(item_queue(P, t, g, p0), cost)], 1);
     }
   }
   __syncthreads();
-  const int b = kCostBins - 1 - tid;  // thread tid owns bucket b (descending order)
+  // exclusive scan of the kQueues * kCostBins counters, kFlat per thread
+  constexpr int kFlat = kQueues * kCostBins / NT;
+  int loc[kFlat];
+  int sum = 0;
+#pragma unroll
+  for (int k = 0; k < kFlat; ++k) {
+    loc[k] = bins[tid * kFlat + k];
+    sum += loc[k];
+  }
   int total;
-  const int start = block_excl_scan<NT>(bins[b], tmp, &total);
-  bins[b] = start;
+  int run = block_excl_scan<NT>(sum, tmp, &total);
+#pragma unroll
+  for (int k = 0; k < kFlat; ++k) {
+    const int f = tid * kFlat + k;
+    bins[f] = run;
+    if (f % kCostBins == 0) P.hdr->qstart[f / kCostBins] = (uint32_t)run;
+    run += loc[k];
+  }
+  __syncthreads();
+  if (tid < kQueues) {
+    const uint32_t end = tid + 1 < kQueues ? (uint32_t)bins[(tid + 1) * kCostBins] : (uint32_t)total;
+    P.hdr->qcount[tid] = end - (uint32_t)bins[tid * kCostBins];
+    P.hdr->next[tid] = 0u;
+  }
   __syncthreads();
   for (int t = tid; t < T; t += NT) {
     const int n = P.tiles[t].nlist;
@@ -291,15 +331,30 @@ __global__ void __launch_bounds__(kItemThreads) plan_items_kernel(PlanParams P) 
     for (int s = 0; s < ns; ++s) {
       const int p0 = piece_start(n, ns, s);
       const int p1 = piece_start(n, ns, s + 1);
-      const int pos = atomicAdd(&bins[min(p1 - p0, kCostBins - 1)], H);
-      for (int g = 0; g < H; ++g) P.items[pos + g] = Item{t, p0, p1, pack_gsn(g, s, ns)};
+      for (int g = 0; g < H; ++g) {
+        const int pos = atomicAdd(&bins[bin_index(item_queue(P, t, g, p0), p1 - p0)], 1);
+        P.items[pos] = Item{t, p0, p1, pack_gsn(g, s, ns)};
+      }
     }
   }
-  for (int i = tid; i < T * H; i += NT) P.arrive[i] = 0u;
+
+  // ---- split (tile, head) groups for the merge kernel
+  int group_base = 0;
+  for (int t0 = 0; t0 < T; t0 += NT) {
+    const int t = t0 + tid;
+    const int ns = t < T ? P.tiles[t].nsplit : 0;
+    int tot;
+    const int off = block_excl_scan<NT>(ns > 1 ? H : 0, tmp, &tot);
+    if (ns > 1) {
+      const int slot0 = P.tiles[t].slot0;
+      for (int g = 0; g < H; ++g) P.groups[group_base + off + g] = Group{t, g, ns, slot0 + g * ns};
+    }
+    group_base += tot;
+  }
   if (tid == 0) {
-    P.hdr->next_item = 0u;
     P.hdr->num_items = (uint32_t)total;
     P.hdr->chunk = (uint32_t)chunk;
+    P.hdr->num_groups = (uint32_t)group_base;
   }
 }
 
