@@ -6,88 +6,379 @@
 // its dot products with the already-rotated queries; V is used as stored.
 // §3.2.1 gives the score (R_t q_t)^T (R_pi(j) k~_j) / sqrt(d).
 //
-// Persistent kernel: about one work-group per CU; each work-group takes work
-// items (q tile, KV head, piece of the tile's visible-block list) from an
-// atomic counter until none are left.
+// Persistent kernel: one work-group per CU takes work items (q tile, KV
+// head, piece of the tile's visible-block list) from the per-XCD queues.
 //
-// Layout of one item (one work-group = 8 waves = 256 query rows):
-//   * rows = BQ query tokens x G query heads sharing KV head g (G = Hq/Hkv);
-//     wave w owns rows 32w .. 32w+31, one row per lane pair (l, l+32).
-//   * key tiles of 64 keys = 4 cache blocks from the tile's block list.
+// One work item = 256 query rows = BQ query tokens x G query heads sharing
+// KV head g (G = Hq/Hkv). A work-group has 8/RB waves; wave w owns RB blocks
+// of 32 rows (rows 32 RB w + 32 rb + (l % 32)); every K or V fragment read
+// from LDS feeds RB MFMAs.
+//   * a pipeline step covers 32 keys = 2 cache blocks of the list.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: keys on the M side, queries on
-//     the N side, so lane l holds 16 keys of ONE query per 32x32 block and the
-//     row max / row sum stay inside the lane (plus one exchange with l^32).
-//   * K rows are written to LDS in a permuted order (bits 2 and 3 of the key
-//     index swapped) so that the accumulator of lane l, element i, is key
-//     16(i/8) + 8(l/32) + i%8 of the 32-key block; eight consecutive
-//     accumulator elements then form exactly the bf16x8 B operand of the PV
-//     MFMA O^T += V^T P^T, with no data movement.
-//   * V is cached transposed inside each block ([d][16]), so the V^T A operand
+//     the N side, so lane l holds 16 keys of ONE query and the row max / sum
+//     stay in the lane (plus one exchange with l ^ 32).
+//   * K rows sit in LDS with bits 2 and 3 of the key index swapped, so the
+//     accumulator of lane l, element i, is key 16(i/8) + 8(l/32) + i%8; eight
+//     consecutive elements then are the bf16x8 B operand of O^T += V^T P^T.
+//   * V is cached transposed inside each block ([d][16]): the V^T A operand
 //     is one 16-byte LDS read of 8 consecutive keys.
-//   * The rotation (rotate-half pairing i <-> i + d/2) is applied once per
-//     work-group per tile, in registers between the global load and the LDS
-//     store, and the next tile's loads are in flight during the current
-//     tile's MFMAs (two LDS buffers, one barrier per tile).
-//   * Online softmax in log2 units with a lazily updated running max: the
+//   * Software pipeline, per step s (one barrier per step):
+//       block 1: S(s+1) = K(s+1) Q^T on MFMA  |  P(s) = exp2(S(s) - m) on VALU
+//       block 2: O += V(s) P(s) on MFMA       |  rotate K(s+2) into LDS, store
+//                                                V(s+1), row max of S(s+1)
+//     then the loads of K(s+3), cos/sin(s+3), V(s+2) are issued and the
+//     running max is raised if S(s+1) needs it. The rotation (rotate-half,
+//     i <-> i + d/2) happens once per work item and tile, between the global
+//     load and the LDS store, in fp32 with one rounding to bf16.
+//   * Global loads are buffer loads: a wave's keys always lie in one cache
+//     block, so the block's base address is a scalar and an invalid block
+//     becomes a zero-size buffer whose loads return zeros.
+//   * The element-wise mask runs only on steps where some row does not see
+//     every key (plan_tiles marks fully visible blocks); it is a uniform branch.
+//   * Online softmax in log2 units with a lazily raised running max: the
 //     accumulators are rescaled only when a row max grows by more than 2^8,
 //     which is exact (numerator and denominator share the stale max).
-//   * A tile whose list was cut into pieces: every piece stores (O, m, l) in
-//     fp32 to its slot; merge_kernel combines them afterwards.
+//   * A piece of a split tile stores fp32 (O, m, l) to its slot; the merge
+//     kernel combines the pieces.
 #include "common.h"
 
 namespace minipic {
 
-constexpr int kNT = 512;          // threads per work-group
-constexpr int kRows = 256;        // query rows per work-group
-constexpr int kKT = 64;           // keys per tile
-constexpr int kListMax = 512;     // list entries staged in LDS at a time
+constexpr int kRows = 256;        // query rows per work item
+constexpr int kKT = 32;           // keys per pipeline step
+constexpr int kListMax = 256;     // list entries staged in LDS per pass
+constexpr int kRsrcWord3 = 0x00020000;  // buffer descriptor word 3 (gfx9, raw dword access)
 
-template <int D>
-struct Lds {
-  static constexpr int KSTR = D + 8;     // bf16 elements per K row (16-byte pad)
-  static constexpr int VSTR = kKT + 8;   // bf16 elements per V^T row
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
+}
+
+// Work-group shape: RB row blocks per wave, NT threads; each thread stages one
+// K unit of CW rotate-half pairs (a key's elements [CW c, CW c + CW) and
+// [d/2 + CW c, d/2 + CW c + CW)) and VU 16-byte V pieces per step.
+template <int D, int RB>
+struct Cfg {
+  static constexpr int NT = 512 / RB;
+  static constexpr int CW = RB == 1 ? 4 : 8;
+  static constexpr int KCH = (D / 2) / CW;       // K units per key
+  static constexpr int KUNITS = kKT * KCH;
+  static_assert(KUNITS <= NT, "one K unit per thread");
+  static constexpr int VUNITS = 2 * D * 2;       // 2 blocks x D rows x 2 halves of 8 keys
+  static constexpr int VU = (VUNITS + NT - 1) / NT;
+  static constexpr int KSTR = D + 8;             // bf16 per K row (16-byte pad: conflict-free MFMA reads)
+  static constexpr int VSTR = kKT + 8;           // bf16 per V^T row
   static constexpr int KSZ = kKT * KSTR;
   static constexpr int VSZ = D * VSTR;
 };
 
 __device__ __forceinline__ int key_perm(int k) {
-  // swap bits 2 and 3 (an involution); bits 0, 1, 4, 5 unchanged
+  // swap bits 2 and 3 (an involution); bits 0, 1, 4 unchanged
   return (k & ~0xC) | ((k & 4) << 1) | ((k & 8) >> 1);
 }
 
-template <int D, bool ROPE>
+// Registers of the loads in flight for one step.
+template <int D, int RB>
 struct Stage {
-  static constexpr int KUNITS = kKT * (D / 16);       // (key, chunk pair)
-  static constexpr int KU = (KUNITS + kNT - 1) / kNT;
-  static constexpr int VUNITS = 4 * D * 2;            // (block, d row, half)
-  static constexpr int VU = VUNITS / kNT;
-  u32x4 ka[KU], kb[KU];
-  f32x4 c0[KU], c1[KU], s0[KU], s1[KU];
-  u32x4 v[VU];
+  static constexpr int CW = Cfg<D, RB>::CW;
+  uint32_t ka[CW / 2], kb[CW / 2];   // CW bf16 of each half of the K unit
+  float c[CW], s[CW];                // cos / sin of the unit's CW frequencies
+  u32x4 v[Cfg<D, RB>::VU];
 };
 
-template <int D, int G, bool ROPE>
-__global__ void __launch_bounds__(kNT, 1) attn_bf16_kernel(AttnParams P) {
+// Per-pass state the step helpers need (all wave-uniform).
+template <int D, int RB>
+struct StepCtx {
+  const BlkDesc* lst;   // LDS: list entries of this pass
+  const int* pos_s;     // LDS: logical position of every key of the pass
+  int n_l;              // entries in the pass
+  const __bf16* kc;     // K cache + offset of head g inside a block group
+  const __bf16* vc;     // V cache + offset of head g
+  int64_t group;        // elements per physical block group (all heads)
+  rsrc_t tab;           // cos/sin table
+  __bf16* kl;           // LDS K buffers
+  __bf16* vl;           // LDS V^T buffers
+};
+
+// The lane's query rows.
+template <int RB>
+struct RowInfo {
+  int c[RB], bq[RB], span[RB];
+  bool valid[RB], pdep[RB];
+};
+
+// physical block of list entry e (uniform), or -1 past the list
+template <int D, int RB>
+__device__ __forceinline__ int entry_phys(const StepCtx<D, RB>& cx, int e) {
+  e = __builtin_amdgcn_readfirstlane(e);
+  return e < cx.n_l ? __builtin_amdgcn_readfirstlane(cx.lst[e].phys) : -1;
+}
+
+// Global loads of step j's K unit and its cos/sin rows. Past the list or for
+// an invalid block the buffer is empty and the loads return zeros.
+template <int D, int RB, bool ROPE>
+__device__ __forceinline__ void load_k(const StepCtx<D, RB>& cx, int j, Stage<D, RB>& st) {
+  using C = Cfg<D, RB>;
+  constexpr int CW = C::CW;
+  const int tid = threadIdx.x;
+  const int key = tid / C::KCH, ch = tid % C::KCH;
+  // a wave's K units lie in one block and are all active or all idle: derive
+  // both from the wave's first thread so the buffer descriptor is scalar
+  const int t0 = __builtin_amdgcn_readfirstlane(tid);
+  const int e = 2 * j + t0 / (C::KCH * kBlock);
+  const int off = key % kBlock;
+  const int ph = entry_phys(cx, e);
+  const int bytes = (ph >= 0 && t0 < C::KUNITS) ? kBlock * D * 2 : 0;
+  const rsrc_t r = make_rsrc(cx.kc + (int64_t)(ph < 0 ? 0 : ph) * cx.group, bytes);
+  const int row_b = (off * D + CW * ch) * 2;
+  if constexpr (CW == 8) {
+    const u32x4 a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, row_b, 0, 0));
+    const u32x4 b = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, row_b + D, 0, 0));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { st.ka[i] = a[i]; st.kb[i] = b[i]; }
+  } else {
+    const u32x2 a = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, row_b, 0, 0));
+    const u32x2 b = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, row_b + D, 0, 0));
+#pragma unroll
+    for (int i = 0; i < 2; ++i) { st.ka[i] = a[i]; st.kb[i] = b[i]; }
+  }
+  if (ROPE) {
+    const int pos = cx.pos_s[(e < cx.n_l ? e : 0) * kBlock + off];
+    const int tb = (pos * D + CW * ch) * 4;
+#pragma unroll
+    for (int q = 0; q < CW / 4; ++q) {
+      const f32x4 cv = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(cx.tab, tb + 16 * q, 0, 0));
+      const f32x4 sv =
+          __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(cx.tab, tb + D * 2 + 16 * q, 0, 0));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { st.c[4 * q + i] = cv[i]; st.s[4 * q + i] = sv[i]; }
+    }
+  }
+}
+
+template <int D, int RB>
+__device__ __forceinline__ void load_v(const StepCtx<D, RB>& cx, int j, Stage<D, RB>& st) {
+  using C = Cfg<D, RB>;
+#pragma unroll
+  for (int u = 0; u < C::VU; ++u) {
+    const int unit = threadIdx.x + u * C::NT;
+    const int u0 = __builtin_amdgcn_readfirstlane(unit);   // a wave's pieces share one block
+    const int rem = unit % (2 * D);
+    const int ph = u0 < C::VUNITS ? entry_phys(cx, 2 * j + u0 / (2 * D)) : -1;
+    const rsrc_t r = make_rsrc(cx.vc + (int64_t)(ph < 0 ? 0 : ph) * cx.group, ph >= 0 ? kBlock * D * 2 : 0);
+    st.v[u] = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, ((rem / 2) * kBlock + 8 * (rem % 2)) * 2, 0, 0));
+  }
+}
+
+// Rotate the staged K unit (rotate-half in fp32, one rounding to bf16) and
+// store it to LDS buffer `buf` in the permuted row order.
+template <int D, int RB, bool ROPE>
+__device__ __forceinline__ void store_k(const StepCtx<D, RB>& cx, int buf, const Stage<D, RB>& st) {
+  using C = Cfg<D, RB>;
+  constexpr int CW = C::CW;
+  const int tid = threadIdx.x;
+  if (C::KUNITS < C::NT && tid >= C::KUNITS) return;
+  const int key = tid / C::KCH, ch = tid % C::KCH;
+  uint32_t ra[CW / 2], rb[CW / 2];
+#pragma unroll
+  for (int j = 0; j < CW / 2; ++j) {
+    if (ROPE) {
+      const float a0 = bf16_lo(st.ka[j]), a1 = bf16_hi(st.ka[j]);
+      const float b0 = bf16_lo(st.kb[j]), b1 = bf16_hi(st.kb[j]);
+      const float c0 = st.c[2 * j], c1 = st.c[2 * j + 1];
+      const float s0 = st.s[2 * j], s1 = st.s[2 * j + 1];
+      ra[j] = pack_bf16x2(a0 * c0 - b0 * s0, a1 * c1 - b1 * s1);
+      rb[j] = pack_bf16x2(b0 * c0 + a0 * s0, b1 * c1 + a1 * s1);
+    } else {
+      ra[j] = st.ka[j];
+      rb[j] = st.kb[j];
+    }
+  }
+  __bf16* dst = cx.kl + buf * C::KSZ + key_perm(key) * C::KSTR + CW * ch;
+  if constexpr (CW == 8) {
+    *(u32x4*)dst = u32x4{ra[0], ra[1], ra[2], ra[3]};
+    *(u32x4*)(dst + D / 2) = u32x4{rb[0], rb[1], rb[2], rb[3]};
+  } else {
+    *(u32x2*)dst = u32x2{ra[0], ra[1]};
+    *(u32x2*)(dst + D / 2) = u32x2{rb[0], rb[1]};
+  }
+}
+
+template <int D, int RB>
+__device__ __forceinline__ void store_v(const StepCtx<D, RB>& cx, int buf, const Stage<D, RB>& st) {
+  using C = Cfg<D, RB>;
+#pragma unroll
+  for (int u = 0; u < C::VU; ++u) {
+    const int unit = threadIdx.x + u * C::NT;
+    if (C::VUNITS % C::NT != 0 && unit >= C::VUNITS) continue;
+    const int bk = unit / (2 * D);
+    const int rem = unit % (2 * D);
+    *(u32x4*)(cx.vl + buf * C::VSZ + (rem / 2) * C::VSTR + kBlock * bk + 8 * (rem % 2)) = st.v[u];
+  }
+}
+
+// S^T for the 32 keys in K buffer `buf`, all row blocks of the wave.
+template <int D, int RB>
+__device__ __forceinline__ void qk(const StepCtx<D, RB>& cx, int buf, const bf16x8 (&qf)[RB][D / 16], f32x16 (&s)[RB]) {
+  using C = Cfg<D, RB>;
+  const int lane = threadIdx.x & 63;
+  const __bf16* kb_ = cx.kl + buf * C::KSZ + (lane & 31) * C::KSTR + 8 * (lane >> 5);
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) s[rb] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const bf16x8 a = *(const bf16x8*)(kb_ + 16 * ks);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[rb][ks], s[rb], 0, 0, 0);
+  }
+}
+
+// O^T += V^T P^T for the 32 keys in V buffer `buf`, all row blocks of the wave.
+template <int D, int RB>
+__device__ __forceinline__ void pv(const StepCtx<D, RB>& cx, int buf, const bf16x8 (&pk)[RB][2],
+                                   f32x16 (&o)[RB][D / 32]) {
+  using C = Cfg<D, RB>;
+  const int lane = threadIdx.x & 63;
+  const __bf16* vb_ = cx.vl + buf * C::VSZ + (lane & 31) * C::VSTR + 8 * (lane >> 5);
+#pragma unroll
+  for (int dg = 0; dg < D / 32; ++dg)
+#pragma unroll
+    for (int sh = 0; sh < 2; ++sh) {
+      const bf16x8 a = *(const bf16x8*)(vb_ + 32 * dg * C::VSTR + 16 * sh);
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) o[rb][dg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[rb][sh], o[rb][dg], 0, 0, 0);
+    }
+}
+
+// true when every row of the tile sees every key of step j (uniform)
+template <int D, int RB>
+__device__ __forceinline__ bool step_full(const StepCtx<D, RB>& cx, int j) {
+  const int e = 2 * j;
+  const int f = (e + 1 < cx.n_l) ? (cx.lst[e].full & cx.lst[e + 1].full) : 0;
+  return __builtin_amdgcn_readfirstlane(f) != 0;
+}
+
+// element-wise mask of step j: block visibility and the causal diagonal
+template <int D, int RB>
+__device__ __forceinline__ void apply_mask(const StepCtx<D, RB>& cx, int j, const RowInfo<RB>& rows, f32x16 (&s)[RB]) {
+  const int h = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int bk = 0; bk < 2; ++bk) {
+    const int e = 2 * j + bk;
+    const bool ev = e < cx.n_l;
+    const BlkDesc bd = cx.lst[ev ? e : 0];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const bool vis = ev && rows.valid[rb] &&
+                       block_visible(bd.kb, bd.span, bd.flags, rows.bq[rb], rows.span[rb], rows.pdep[rb]);
+      const int lim = rows.c[rb] - bd.kb * kBlock - 8 * h;
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        if (!(vis && r <= lim)) s[rb][8 * bk + r] = -INFINITY;
+    }
+  }
+}
+
+// P = exp2(S * scale_log2 - m) rounded to bf16 in the B-operand layout of the
+// PV MFMA; the row sums accumulate in fp32.
+template <int RB>
+__device__ __forceinline__ void softmax_p(const f32x16 (&s)[RB], float sl2, const float (&m_run)[RB],
+                                          float (&l_run)[RB], bf16x8 (&pk)[RB][2]) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const float m_use = (m_run[rb] == -INFINITY) ? 0.f : m_run[rb];
+#pragma unroll
+    for (int sh = 0; sh < 2; ++sh) {
+      u32x4 u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[rb][8 * sh + 2 * j], sl2, -m_use));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[rb][8 * sh + 2 * j + 1], sl2, -m_use));
+        u[j] = pack_bf16x2(p0, p1);
+        l_run[rb] += p0 + p1;
+      }
+      pk[rb][sh] = __builtin_bit_cast(bf16x8, u);
+    }
+  }
+}
+
+// Raise the running max where the scores of the coming step need it
+// (lazily: only when a row max grows by more than 2^8).
+template <int D, int RB>
+__device__ __forceinline__ void raise_max(const f32x16 (&s)[RB], float sl2, float (&m_run)[RB], float (&l_run)[RB],
+                                          f32x16 (&o)[RB][D / 32]) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    float mx = s[rb][0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[rb][i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float ms = mx * sl2;
+    if (__any(ms > m_run[rb] + 8.0f)) {
+      const float m_new = fmaxf(m_run[rb], ms);
+      const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run[rb] - m_new);
+#pragma unroll
+      for (int dg = 0; dg < D / 32; ++dg)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[rb][dg][i] *= alpha;
+      l_run[rb] *= alpha;
+      m_run[rb] = m_new;
+    }
+  }
+}
+
+// Instruction-scheduling hint for one pipeline step (masks of
+// __builtin_amdgcn_sched_group_barrier: 0x008 MFMA, 0x002 VALU, 0x100 LDS
+// read, 0x200 LDS write, 0x020 global read): the QK^T MFMAs of the next step
+// interleaved with the softmax VALU work of this one, then the PV MFMAs
+// interleaved with the rotation, the LDS stores and the next loads; operand
+// reads from LDS run two MFMAs ahead.
+template <int NQK, int NPV>
+__device__ __forceinline__ void sched_step() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+  for (int i = 0; i < NQK; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < NPV; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i + 2 < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+  }
+}
+
+template <int D, int G, bool ROPE, int RB>
+__global__ void __launch_bounds__(512 / RB, 1) attn_bf16_kernel(AttnParams P) {
+  using C = Cfg<D, RB>;
+  using St = Stage<D, RB>;
+  constexpr int NT = C::NT;
   constexpr int BQ = kRows / G;
-  using L = Lds<D>;
-  using St = Stage<D, ROPE>;
+  constexpr int NKS = D / 16;             // k-steps of QK^T
+  constexpr int NDG = D / 32;             // 32-row d blocks of O^T
   __shared__ BlkDesc lst[kListMax];
+  __shared__ int pos_s[ROPE ? kListMax * kBlock : 1];
   __shared__ int s_next;
-  __shared__ __attribute__((aligned(16))) __bf16 kl[2 * L::KSZ];
-  __shared__ __attribute__((aligned(16))) __bf16 vl[2 * L::VSZ];
+  __shared__ __attribute__((aligned(16))) __bf16 kl[2 * C::KSZ];
+  __shared__ __attribute__((aligned(16))) __bf16 vl[2 * C::VSZ];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int l32 = lane & 31;
   const int h = lane >> 5;
-  const int row = 32 * w + l32;   // this lane's query row within the item
-  const int tok = row / G;
-  const int hig = row % G;
 
   const __bf16* kc = (const __bf16*)P.k_cache;
   const __bf16* vc = (const __bf16*)P.v_cache;
   const float sl2 = P.scale_log2;
+  const rsrc_t tab = make_rsrc(P.cos_sin, P.max_pos * D * 4);
+
   int it = next_item(P.hdr, &s_next);
   while (it >= 0) {
     if (tid == 0) s_next = claim_item(P.hdr);  // the following item
@@ -96,28 +387,32 @@ __global__ void __launch_bounds__(kNT, 1) attn_bf16_kernel(AttnParams P) {
     const int sp = (item.gsn >> 8) & 0xfff;
     const int ns = item.gsn >> 20;
     const TileDesc td = P.tiles[item.tile];
-    const TokDesc tk = P.toks[(int64_t)item.tile * BQ + tok];
-    const bool rvalid = tok < td.nq && tk.c >= 0;
-    const int c_row = rvalid ? tk.c : -1;
-    const int bq_row = rvalid ? (c_row >> 4) : -1;
-    const int span_row = tk.span;
-    const bool pdep_row = rvalid && tk.pdep;
-    const int head = g * G + hig;
-    const int64_t qrow = (int64_t)td.row0 + tok;
     const int32_t* lpos = P.logical_pos + (int64_t)td.r * P.max_blocks * kBlock;
     const BlkDesc* blist = P.blist + (int64_t)item.tile * P.max_blocks;
+    const int64_t kv_head = (int64_t)g * kBlock * D;   // offset of head g inside a block group
 
-    // ---- this lane's query row (B operand of S^T = K Q^T)
-    bf16x8 qf[D / 16];
-    {
-      const __bf16* qp = (const __bf16*)P.q + (qrow * P.hq + head) * D;
+    // ---- the lane's query rows
+    RowInfo<RB> rows;
+    int row[RB];
+    int64_t qoff[RB];
+    bf16x8 qf[RB][NKS];
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        if (rvalid) qf[ks] = *(const bf16x8*)(qp + 16 * ks + 8 * h);
-        else qf[ks] = bf16x8{};
-      }
-      if ((P.flags & MINIPIC_FLAG_ROTATE_Q) && rvalid) {
-        int pos = lpos[c_row];
+    for (int rb = 0; rb < RB; ++rb) {
+      row[rb] = 32 * RB * w + 32 * rb + l32;
+      const int tok = row[rb] / G;
+      const TokDesc tk = P.toks[(int64_t)item.tile * BQ + tok];
+      const bool valid = tok < td.nq && tk.c >= 0;
+      rows.valid[rb] = valid;
+      rows.c[rb] = valid ? tk.c : -1;
+      rows.bq[rb] = valid ? (tk.c >> 4) : -1;
+      rows.span[rb] = tk.span;
+      rows.pdep[rb] = valid && tk.pdep;
+      qoff[rb] = (((int64_t)td.row0 + tok) * P.hq + g * G + row[rb] % G) * D;
+      const __bf16* qp = (const __bf16*)P.q + qoff[rb];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) qf[rb][ks] = valid ? *(const bf16x8*)(qp + 16 * ks + 8 * h) : bf16x8{};
+      if ((P.flags & MINIPIC_FLAG_ROTATE_Q) && valid) {
+        int pos = lpos[tk.c];
         if (pos < 0 || pos >= P.max_pos) {
           atomicOr(&P.hdr->err, (uint32_t)MINIPIC_EW_POS);
           pos = pos < 0 ? 0 : P.max_pos - 1;
@@ -125,9 +420,9 @@ __global__ void __launch_bounds__(kNT, 1) attn_bf16_kernel(AttnParams P) {
         const float* cs = P.cos_sin + (int64_t)pos * D;
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks) {
-          const u32x4 a = __builtin_bit_cast(u32x4, qf[ks]);
-          const u32x4 b = __builtin_bit_cast(u32x4, qf[ks + D / 32]);
-          u32x4 ra, rb;
+          const u32x4 a = __builtin_bit_cast(u32x4, qf[rb][ks]);
+          const u32x4 b = __builtin_bit_cast(u32x4, qf[rb][ks + D / 32]);
+          u32x4 ra, rbv;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int i0 = 16 * ks + 8 * h + 2 * j;
@@ -136,235 +431,125 @@ __global__ void __launch_bounds__(kNT, 1) attn_bf16_kernel(AttnParams P) {
             const float a0 = bf16_lo(a[j]), a1 = bf16_hi(a[j]);
             const float b0 = bf16_lo(b[j]), b1 = bf16_hi(b[j]);
             ra[j] = pack_bf16x2(a0 * c_0 - b0 * s_0, a1 * c_1 - b1 * s_1);
-            rb[j] = pack_bf16x2(b0 * c_0 + a0 * s_0, b1 * c_1 + a1 * s_1);
+            rbv[j] = pack_bf16x2(b0 * c_0 + a0 * s_0, b1 * c_1 + a1 * s_1);
           }
-          qf[ks] = __builtin_bit_cast(bf16x8, ra);
-          qf[ks + D / 32] = __builtin_bit_cast(bf16x8, rb);
+          qf[rb][ks] = __builtin_bit_cast(bf16x8, ra);
+          qf[rb][ks + D / 32] = __builtin_bit_cast(bf16x8, rbv);
         }
       }
     }
 
-    f32x16 o[D / 32];
+    f32x16 o[RB][NDG];
 #pragma unroll
-    for (int i = 0; i < D / 32; ++i) o[i] = f32x16{};
-    float m_run = -INFINITY;   // running max of scaled scores (log2 units)
-    float l_run = 0.f;         // this half-lane's share of the row sum
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < NDG; ++i) o[rb][i] = f32x16{};
+    float m_run[RB], l_run[RB];   // running max of scaled scores (log2 units); half-lane row sums
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      m_run[rb] = -INFINITY;
+      l_run[rb] = 0.f;
+    }
 
     for (int c0 = item.p0; c0 < item.p1; c0 += kListMax) {
       const int n_l = min(kListMax, item.p1 - c0);
-      for (int i = tid; i < n_l; i += kNT) lst[i] = blist[c0 + i];
+      const int nsteps = (n_l + 1) / 2;
+      // ---- stage the list piece and the keys' logical positions
+      for (int i = tid; i < n_l; i += NT) lst[i] = blist[c0 + i];
       __syncthreads();
-      const int ntiles = (n_l + 3) / 4;
-
-      auto load = [&](int ti, St& st) {
-#pragma unroll
-        for (int u = 0; u < St::KU; ++u) {
-          const int unit = tid + u * kNT;
-          st.ka[u] = u32x4{}; st.kb[u] = u32x4{};
-          if (ROPE) { st.c0[u] = f32x4{}; st.c1[u] = f32x4{}; st.s0[u] = f32x4{}; st.s1[u] = f32x4{}; }
-          if (unit < St::KUNITS) {
-            const int key = unit / (D / 16);
-            const int cp = unit % (D / 16);
-            const int e = 4 * ti + key / kBlock;
-            const int off = key % kBlock;
-            const int ph = e < n_l ? lst[e].phys : -1;
-            if (ph >= 0) {
-              const __bf16* kr = kc + (((int64_t)ph * P.hkv + g) * kBlock + off) * D;
-              st.ka[u] = *(const u32x4*)(kr + 8 * cp);
-              st.kb[u] = *(const u32x4*)(kr + D / 2 + 8 * cp);
-              if (ROPE) {
-                const int pos0 = lst[e].pos0;
-                int pos = pos0 >= 0 ? pos0 + off : lpos[lst[e].kb * kBlock + off];
-                if (pos < 0 || pos >= P.max_pos) {
-                  atomicOr(&P.hdr->err, (uint32_t)MINIPIC_EW_POS);
-                  pos = pos < 0 ? 0 : P.max_pos - 1;
-                }
-                const float* cs = P.cos_sin + (int64_t)pos * D + 8 * cp;
-                st.c0[u] = *(const f32x4*)(cs);
-                st.c1[u] = *(const f32x4*)(cs + 4);
-                st.s0[u] = *(const f32x4*)(cs + D / 2);
-                st.s1[u] = *(const f32x4*)(cs + D / 2 + 4);
-              }
-            }
+      if (ROPE) {
+        for (int i = tid; i < n_l * kBlock; i += NT) {
+          const BlkDesc bd = lst[i / kBlock];
+          int pos = bd.pos0 >= 0 ? bd.pos0 + i % kBlock : lpos[bd.kb * kBlock + i % kBlock];
+          if (pos < 0 || pos >= P.max_pos) {
+            atomicOr(&P.hdr->err, (uint32_t)MINIPIC_EW_POS);
+            pos = pos < 0 ? 0 : P.max_pos - 1;
           }
+          pos_s[i] = pos;
         }
-#pragma unroll
-        for (int u = 0; u < St::VU; ++u) {
-          const int unit = tid + u * kNT;
-          const int b = unit / (2 * D);
-          const int rem = unit % (2 * D);
-          const int e = 4 * ti + b;
-          const int ph = e < n_l ? lst[e].phys : -1;
-          st.v[u] = u32x4{};
-          if (ph >= 0)
-            st.v[u] = *(const u32x4*)(vc + (((int64_t)ph * P.hkv + g) * D + rem / 2) * kBlock + 8 * (rem % 2));
-        }
-      };
+        __syncthreads();
+      }
 
-      auto store = [&](int buf, const St& st) {
-        __bf16* kb_ = kl + buf * L::KSZ;
-        __bf16* vb_ = vl + buf * L::VSZ;
-#pragma unroll
-        for (int u = 0; u < St::KU; ++u) {
-          const int unit = tid + u * kNT;
-          if (unit < St::KUNITS) {
-            const int key = unit / (D / 16);
-            const int cp = unit % (D / 16);
-            u32x4 ra = st.ka[u], rb = st.kb[u];
-            if (ROPE) {
-              const float cc[8] = {st.c0[u][0], st.c0[u][1], st.c0[u][2], st.c0[u][3],
-                                   st.c1[u][0], st.c1[u][1], st.c1[u][2], st.c1[u][3]};
-              const float ss[8] = {st.s0[u][0], st.s0[u][1], st.s0[u][2], st.s0[u][3],
-                                   st.s1[u][0], st.s1[u][1], st.s1[u][2], st.s1[u][3]};
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const float a0 = bf16_lo(st.ka[u][j]), a1 = bf16_hi(st.ka[u][j]);
-                const float b0 = bf16_lo(st.kb[u][j]), b1 = bf16_hi(st.kb[u][j]);
-                const float c_0 = cc[2 * j], c_1 = cc[2 * j + 1];
-                const float s_0 = ss[2 * j], s_1 = ss[2 * j + 1];
-                ra[j] = pack_bf16x2(a0 * c_0 - b0 * s_0, a1 * c_1 - b1 * s_1);
-                rb[j] = pack_bf16x2(b0 * c_0 + a0 * s_0, b1 * c_1 + a1 * s_1);
-              }
-            }
-            __bf16* dst = kb_ + key_perm(key) * L::KSTR + 8 * cp;
-            *(u32x4*)dst = ra;
-            *(u32x4*)(dst + D / 2) = rb;
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < St::VU; ++u) {
-          const int unit = tid + u * kNT;
-          const int b = unit / (2 * D);
-          const int rem = unit % (2 * D);
-          *(u32x4*)(vb_ + (rem / 2) * L::VSTR + kBlock * b + 8 * (rem % 2)) = st.v[u];
-        }
-      };
+      StepCtx<D, RB> cx;
+      cx.lst = lst;
+      cx.pos_s = pos_s;
+      cx.n_l = n_l;
+      cx.kc = kc + kv_head;
+      cx.vc = vc + kv_head;
+      cx.group = (int64_t)P.hkv * kBlock * D;
+      cx.tab = tab;
+      cx.kl = kl;
+      cx.vl = vl;
 
+      // ---- prologue: K(0), V(0), K(1) in LDS; S(0); loads of K(2), V(1) in flight
       St st;
-      load(0, st);
-      store(0, st);
+      load_k<D, RB, ROPE>(cx, 0, st);
+      load_v<D, RB>(cx, 0, st);
+      store_k<D, RB, ROPE>(cx, 0, st);
+      store_v<D, RB>(cx, 0, st);
+      load_k<D, RB, ROPE>(cx, 1, st);
+      store_k<D, RB, ROPE>(cx, 1, st);
       __syncthreads();
-      for (int ti = 0; ti < ntiles; ++ti) {
-        const int buf = ti & 1;
-        const bool more = ti + 1 < ntiles;
-        if (more) load(ti + 1, st);
+      f32x16 s_cur[RB];
+      qk<D, RB>(cx, 0, qf, s_cur);
+      if (!step_full(cx, 0)) apply_mask(cx, 0, rows, s_cur);
+      raise_max<D, RB>(s_cur, sl2, m_run, l_run, o);
+      load_k<D, RB, ROPE>(cx, 2, st);
+      load_v<D, RB>(cx, 1, st);
 
-        // ---- S^T = K Q^T for the 64-key tile
-        const __bf16* kb_ = kl + buf * L::KSZ;
-        f32x16 sacc[2];
+      for (int s = 0; s < nsteps; ++s) {
+        // ---- one branch-free region: S(s+1) and O += V(s) P(s) on MFMA;
+        // P(s), the rotation of K(s+2) and the stores of K(s+2), V(s+1) on
+        // VALU / LDS; the loads of step s+3 issued at the end
+        f32x16 s_nxt[RB];
+        qk<D, RB>(cx, (s + 1) & 1, qf, s_nxt);
+        bf16x8 pk[RB][2];
+        softmax_p<RB>(s_cur, sl2, m_run, l_run, pk);
+        pv<D, RB>(cx, s & 1, pk, o);
+        store_k<D, RB, ROPE>(cx, s & 1, st);
+        store_v<D, RB>(cx, (s + 1) & 1, st);
+        load_k<D, RB, ROPE>(cx, s + 3, st);
+        load_v<D, RB>(cx, s + 2, st);
+        sched_step<RB * NKS, RB * 2 * NDG>();
+        // ---- S(s+1): mask where needed, raise the running max
+        if (!step_full(cx, s + 1)) apply_mask(cx, s + 1, rows, s_nxt);
+        raise_max<D, RB>(s_nxt, sl2, m_run, l_run, o);
 #pragma unroll
-        for (int kb32 = 0; kb32 < 2; ++kb32) {
-          sacc[kb32] = f32x16{};
-#pragma unroll
-          for (int ks = 0; ks < D / 16; ++ks) {
-            const bf16x8 a = *(const bf16x8*)(kb_ + (32 * kb32 + l32) * L::KSTR + 16 * ks + 8 * h);
-            sacc[kb32] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], sacc[kb32], 0, 0, 0);
-          }
-        }
-
-        // ---- block mask (block-granular + causal diagonal)
-        bool vis[4];
-        int lim[4];
-        bool full = true;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int e = 4 * ti + b;
-          const bool ev = e < n_l;
-          const BlkDesc bd = ev ? lst[e] : BlkDesc{0, -1, 0, 0, -1, 0, 0, 0};
-          vis[b] = ev && rvalid && block_visible(bd.kb, bd.span, bd.flags, bq_row, span_row, pdep_row);
-          lim[b] = c_row - bd.kb * kBlock - 8 * h;
-          full = full && vis[b] && lim[b] >= 7;
-        }
-        if (!__all(full)) {
-#pragma unroll
-          for (int kb32 = 0; kb32 < 2; ++kb32)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int b = 2 * kb32 + i / 8;
-              if (!(vis[b] && (i % 8) <= lim[b])) sacc[kb32][i] = -INFINITY;
-            }
-        }
-
-        // ---- online softmax (log2 units, lazy rescale)
-        float mx = sacc[0][0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[0][i]);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[1][i]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float ms = mx * sl2;
-        if (__any(ms > m_run + 8.0f)) {
-          const float m_new = fmaxf(m_run, ms);
-          const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
-#pragma unroll
-          for (int dg = 0; dg < D / 32; ++dg)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) o[dg][i] *= alpha;
-          l_run *= alpha;
-          m_run = m_new;
-        }
-        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-        bf16x8 pk[2][2];
-#pragma unroll
-        for (int kb32 = 0; kb32 < 2; ++kb32)
-#pragma unroll
-          for (int sh = 0; sh < 2; ++sh) {
-            u32x4 u;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb32][8 * sh + 2 * j], sl2, -m_use));
-              const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb32][8 * sh + 2 * j + 1], sl2, -m_use));
-              u[j] = pack_bf16x2(p0, p1);
-              l_run += p0 + p1;
-            }
-            pk[kb32][sh] = __builtin_bit_cast(bf16x8, u);
-          }
-
-        // ---- O^T += V^T P^T
-        const __bf16* vb_ = vl + buf * L::VSZ;
-#pragma unroll
-        for (int dg = 0; dg < D / 32; ++dg)
-#pragma unroll
-          for (int kb32 = 0; kb32 < 2; ++kb32)
-#pragma unroll
-            for (int sh = 0; sh < 2; ++sh) {
-              const bf16x8 a = *(const bf16x8*)(vb_ + (32 * dg + l32) * L::VSTR + 32 * kb32 + 16 * sh + 8 * h);
-              o[dg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[kb32][sh], o[dg], 0, 0, 0);
-            }
-
-        if (more) store(buf ^ 1, st);
+        for (int rb = 0; rb < RB; ++rb) s_cur[rb] = s_nxt[rb];
         __syncthreads();
       }
     }
 
     // ---- epilogue
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-    __bf16* op = (__bf16*)P.out + (qrow * P.hq + head) * D;
-    if (ns == 1) {
-      if (rvalid) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const float l_tot = l_run[rb] + __shfl_xor(l_run[rb], 32, 64);
+      if (!rows.valid[rb]) continue;
+      if (ns == 1) {
+        __bf16* op = (__bf16*)P.out + qoff[rb];
         const float inv = 1.f / l_tot;
 #pragma unroll
-        for (int dg = 0; dg < D / 32; ++dg)
+        for (int dg = 0; dg < NDG; ++dg)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             u32x2 u;
-            u[0] = pack_bf16x2(o[dg][4 * j] * inv, o[dg][4 * j + 1] * inv);
-            u[1] = pack_bf16x2(o[dg][4 * j + 2] * inv, o[dg][4 * j + 3] * inv);
+            u[0] = pack_bf16x2(o[rb][dg][4 * j] * inv, o[rb][dg][4 * j + 1] * inv);
+            u[1] = pack_bf16x2(o[rb][dg][4 * j + 2] * inv, o[rb][dg][4 * j + 3] * inv);
             *(u32x2*)(op + 32 * dg + 8 * j + 4 * h) = u;
           }
+      } else {
+        // a piece of a split tile: fp32 partial result to its slot (merged by merge_kernel)
+        const int64_t pr = (int64_t)(td.slot0 + g * ns + sp) * kRows + row[rb];
+        float* po = P.part_o + pr * D;
+#pragma unroll
+        for (int dg = 0; dg < NDG; ++dg)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const f32x4 u = {o[rb][dg][4 * j], o[rb][dg][4 * j + 1], o[rb][dg][4 * j + 2], o[rb][dg][4 * j + 3]};
+            *(f32x4*)(po + 32 * dg + 8 * j + 4 * h) = u;
+          }
+        if (h == 0) P.part_ml[pr] = make_float2(m_run[rb], l_tot);
       }
-    } else if (rvalid) {
-      // a piece of a split tile: fp32 partial result to its slot (merged by merge_kernel)
-      const int64_t pr = (int64_t)(td.slot0 + g * ns + sp) * kRows + row;
-      float* po = P.part_o + pr * D;
-#pragma unroll
-      for (int dg = 0; dg < D / 32; ++dg)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f32x4 u = {o[dg][4 * j], o[dg][4 * j + 1], o[dg][4 * j + 2], o[dg][4 * j + 3]};
-          *(f32x4*)(po + 32 * dg + 8 * j + 4 * h) = u;
-        }
-      if (h == 0) P.part_ml[pr] = make_float2(m_run, l_tot);
     }
     __syncthreads();
     it = __builtin_amdgcn_readfirstlane(s_next);
@@ -372,9 +557,14 @@ __global__ void __launch_bounds__(kNT, 1) attn_bf16_kernel(AttnParams P) {
   }
 }
 
+#ifndef MINIPIC_RB
+#define MINIPIC_RB 1
+#endif
+constexpr int kRB = MINIPIC_RB;   // row blocks per wave of the built kernels
+
 template <int D, int G, bool ROPE>
 static hipError_t launch_one(const AttnParams& p, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((attn_bf16_kernel<D, G, ROPE>), dim3((unsigned)grid), dim3(kNT), 0, s, p);
+  hipLaunchKernelGGL((attn_bf16_kernel<D, G, ROPE, kRB>), dim3((unsigned)grid), dim3(512 / kRB), 0, s, p);
   return hipGetLastError();
 }
 
@@ -400,9 +590,9 @@ hipError_t launch_attn_bf16(const AttnParams& p, int D, int G, bool rope, int gr
 int attn_bf16_blocks_per_cu(int D, int G, bool rope) {
   int n = 0;
   hipError_t e = hipErrorInvalidValue;
-#define MINIPIC_OCC(DD, GG, RR)                                                                   \
-  if (D == DD && G == GG && rope == RR)                                                          \
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<DD, GG, RR>, kNT, 0);
+#define MINIPIC_OCC(DD, GG, RR)                                                                          \
+  if (D == DD && G == GG && rope == RR)                                                                 \
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<DD, GG, RR, kRB>, 512 / kRB, 0);
   MINIPIC_OCC(128, 1, true) MINIPIC_OCC(128, 2, true) MINIPIC_OCC(128, 4, true) MINIPIC_OCC(128, 8, true)
   MINIPIC_OCC(128, 1, false) MINIPIC_OCC(128, 2, false) MINIPIC_OCC(128, 4, false) MINIPIC_OCC(128, 8, false)
   MINIPIC_OCC(64, 1, true) MINIPIC_OCC(64, 2, true) MINIPIC_OCC(64, 4, true) MINIPIC_OCC(64, 8, true)

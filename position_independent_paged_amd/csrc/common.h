@@ -105,7 +105,9 @@ struct BlkDesc {
   int32_t pos0;    // if >= 0: the block's logical positions are pos0 .. pos0+15, all
                    // inside the cos/sin table (key offset k sits at pos0 + k); -1: look
                    // each key's position up in logical_pos
-  int32_t pad0, pad1, pad2;
+  int32_t full;    // 1: every query row of the tile sees every key of the block (the
+                   // block lies below each row's own block and is visible to each row)
+  int32_t pad1, pad2;
 };
 
 // One unit of attention work: KV head g of tile `tile`, list entries [p0, p1).

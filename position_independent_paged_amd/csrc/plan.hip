@@ -23,7 +23,7 @@ namespace minipic {
 // (those of its tokens below L) run pos0, pos0+1, ... and the whole run
 // pos0 .. pos0+15 lies inside the cos/sin table.
 __device__ __forceinline__ BlkDesc make_blk(const PlanParams& P, const int32_t* btab, const int32_t* lpos, int L,
-                                            int kb, int span, int flags) {
+                                            int kb, int span, int flags, int full) {
   int ph = btab[kb];
   if (ph < 0 || (int64_t)ph >= P.num_blocks) {
     atomicOr(&P.hdr->err, (uint32_t)MINIPIC_EW_BLOCK);
@@ -43,7 +43,7 @@ __device__ __forceinline__ BlkDesc make_blk(const PlanParams& P, const int32_t* 
   bool cons = p[0] >= 0 && p[0] <= P.max_pos - kBlock;
 #pragma unroll
   for (int k = 1; k < kBlock; ++k) cons = cons && (k >= nvalid || p[k] == p[0] + k);
-  return BlkDesc{kb, ph, span, flags, cons ? p[0] : -1, 0, 0, 0};
+  return BlkDesc{kb, ph, span, flags, cons ? p[0] : -1, full, 0, 0};
 }
 
 template <int BQ>
@@ -170,30 +170,26 @@ __global__ void __launch_bounds__(kPlanThreads) plan_tiles_kernel(PlanParams P) 
     const bool is = (f & MINIPIC_BLK_GLOBAL) != 0;
     int tot;
     const int i = block_excl_scan_pred<NT>(is, tmp, &tot);
-    if (is) out[n + i] = make_blk(P, btab, lpos, L, kb, span[kb], f);
+    if (is) out[n + i] = make_blk(P, btab, lpos, L, kb, span[kb], f, 1);  // below every query block
     n += tot;
   }
   for (int base = lo; base <= hi; base += NT) {
     const int kb = base + tid;
-    bool vis = false;
+    bool vis = false, full = true;
     int f = 0, s = 0;
     if (kb <= hi) {
       f = flg[kb];
       s = span[kb];
-      if (anyp && kb <= phi) {
-        vis = true;
-      } else {
-        for (int e = 0; e < n_e; ++e) {
-          if (kb <= e_bq[e] && (e_pdep[e] || (f & MINIPIC_BLK_GLOBAL) || e_span[e] == s)) {
-            vis = true;
-            break;
-          }
-        }
+      // visible to some row (vis) / to every row, strictly below its own block (full)
+      for (int e = 0; e < n_e; ++e) {
+        const bool see = kb <= e_bq[e] && (e_pdep[e] || (f & MINIPIC_BLK_GLOBAL) || e_span[e] == s);
+        vis = vis || see;
+        full = full && see && kb < e_bq[e];
       }
     }
     int tot;
     const int i = block_excl_scan_pred<NT>(vis, tmp, &tot);
-    if (vis) out[n + i] = make_blk(P, btab, lpos, L, kb, s, f);
+    if (vis) out[n + i] = make_blk(P, btab, lpos, L, kb, s, f, full ? 1 : 0);
     n += tot;
   }
   if (tid == 0) *td = TileDesc{r, row0, nq, n, 0, -1, 0, 0};
