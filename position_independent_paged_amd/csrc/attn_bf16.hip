@@ -37,7 +37,9 @@
 //     every key (plan_tiles marks fully visible blocks); it is a uniform branch.
 //   * Online softmax in log2 units with a lazily raised running max: the
 //     accumulators are rescaled only when a row max grows by more than 2^8,
-//     which is exact (numerator and denominator share the stale max).
+//     which is exact (numerator and denominator share the stale max). The
+//     row sums come from the PV MFMA itself (a constant all-ones A row), so
+//     they sum the same bf16 P as the numerator and cost no VALU adds.
 //   * A piece of a split tile stores fp32 (O, m, l) to its slot; the merge
 //     kernel combines the pieces.
 #include "common.h"
@@ -47,12 +49,27 @@ namespace minipic {
 constexpr int kRows = 256;        // query rows per work item
 constexpr int kKT = 32;           // keys per pipeline step
 constexpr int kListMax = 256;     // list entries staged in LDS per pass
+// Sentinel entries after the last one of a pass (no block: loads return
+// zeros, never visible, never full), so the look-ups of the steps past the
+// end need no bounds test and the step body stays free of branches.
+constexpr int kListPad = 8;
 constexpr int kRsrcWord3 = 0x00020000;  // buffer descriptor word 3 (gfx9, raw dword access)
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
+}
+
+// Combine a value with the one held by lane l ^ 32: v_permlane32_swap gives
+// both operands' halves, so max / sum of the pair needs no LDS round trip.
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Work-group shape: RB row blocks per wave, NT threads; each thread stages one
@@ -108,11 +125,11 @@ struct RowInfo {
   bool valid[RB], pdep[RB];
 };
 
-// physical block of list entry e (uniform), or -1 past the list
+// physical block of list entry e (uniform; -1 for a sentinel past the list)
 template <int D, int RB>
 __device__ __forceinline__ int entry_phys(const StepCtx<D, RB>& cx, int e) {
   e = __builtin_amdgcn_readfirstlane(e);
-  return e < cx.n_l ? __builtin_amdgcn_readfirstlane(cx.lst[e].phys) : -1;
+  return __builtin_amdgcn_readfirstlane(cx.lst[e].phys);
 }
 
 // Global loads of step j's K unit and its cos/sin rows. Past the list or for
@@ -144,7 +161,7 @@ __device__ __forceinline__ void load_k(const StepCtx<D, RB>& cx, int j, Stage<D,
     for (int i = 0; i < 2; ++i) { st.ka[i] = a[i]; st.kb[i] = b[i]; }
   }
   if (ROPE) {
-    const int pos = cx.pos_s[(e < cx.n_l ? e : 0) * kBlock + off];
+    const int pos = cx.pos_s[e * kBlock + off];
     const int tb = (pos * D + CW * ch) * 4;
 #pragma unroll
     for (int q = 0; q < CW / 4; ++q) {
@@ -165,7 +182,8 @@ __device__ __forceinline__ void load_v(const StepCtx<D, RB>& cx, int j, Stage<D,
     const int unit = threadIdx.x + u * C::NT;
     const int u0 = __builtin_amdgcn_readfirstlane(unit);   // a wave's pieces share one block
     const int rem = unit % (2 * D);
-    const int ph = u0 < C::VUNITS ? entry_phys(cx, 2 * j + u0 / (2 * D)) : -1;
+    const bool act = (C::VU * C::NT == C::VUNITS) || u0 < C::VUNITS;
+    const int ph = act ? entry_phys(cx, 2 * j + u0 / (2 * D)) : -1;
     const rsrc_t r = make_rsrc(cx.vc + (int64_t)(ph < 0 ? 0 : ph) * cx.group, ph >= 0 ? kBlock * D * 2 : 0);
     st.v[u] = __builtin_bit_cast(
         u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, ((rem / 2) * kBlock + 8 * (rem % 2)) * 2, 0, 0));
@@ -235,10 +253,13 @@ __device__ __forceinline__ void qk(const StepCtx<D, RB>& cx, int buf, const bf16
   }
 }
 
-// O^T += V^T P^T for the 32 keys in V buffer `buf`, all row blocks of the wave.
+// O^T += V^T P^T for the 32 keys in V buffer `buf`, all row blocks of the
+// wave. The row sums of P come from the same MFMA with a constant A operand
+// whose first row is all ones: lsum[rb] element 0 of lane l (l < 32) is the
+// running sum of row l, summed from the bf16 P the numerator uses.
 template <int D, int RB>
 __device__ __forceinline__ void pv(const StepCtx<D, RB>& cx, int buf, const bf16x8 (&pk)[RB][2],
-                                   f32x16 (&o)[RB][D / 32]) {
+                                   f32x16 (&o)[RB][D / 32], f32x16 (&lsum)[RB], const bf16x8& ones) {
   using C = Cfg<D, RB>;
   const int lane = threadIdx.x & 63;
   const __bf16* vb_ = cx.vl + buf * C::VSZ + (lane & 31) * C::VSTR + 8 * (lane >> 5);
@@ -250,14 +271,17 @@ __device__ __forceinline__ void pv(const StepCtx<D, RB>& cx, int buf, const bf16
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) o[rb][dg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[rb][sh], o[rb][dg], 0, 0, 0);
     }
+#pragma unroll
+  for (int sh = 0; sh < 2; ++sh)
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) lsum[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pk[rb][sh], lsum[rb], 0, 0, 0);
 }
 
 // true when every row of the tile sees every key of step j (uniform)
 template <int D, int RB>
 __device__ __forceinline__ bool step_full(const StepCtx<D, RB>& cx, int j) {
   const int e = 2 * j;
-  const int f = (e + 1 < cx.n_l) ? (cx.lst[e].full & cx.lst[e + 1].full) : 0;
-  return __builtin_amdgcn_readfirstlane(f) != 0;
+  return __builtin_amdgcn_readfirstlane(cx.lst[e].full & cx.lst[e + 1].full) != 0;
 }
 
 // element-wise mask of step j: block visibility and the causal diagonal
@@ -266,12 +290,10 @@ __device__ __forceinline__ void apply_mask(const StepCtx<D, RB>& cx, int j, cons
   const int h = (threadIdx.x & 63) >> 5;
 #pragma unroll
   for (int bk = 0; bk < 2; ++bk) {
-    const int e = 2 * j + bk;
-    const bool ev = e < cx.n_l;
-    const BlkDesc bd = cx.lst[ev ? e : 0];
+    const BlkDesc bd = cx.lst[2 * j + bk];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const bool vis = ev && rows.valid[rb] &&
+      const bool vis = rows.valid[rb] &&
                        block_visible(bd.kb, bd.span, bd.flags, rows.bq[rb], rows.span[rb], rows.pdep[rb]);
       const int lim = rows.c[rb] - bd.kb * kBlock - 8 * h;
 #pragma unroll
@@ -285,7 +307,7 @@ __device__ __forceinline__ void apply_mask(const StepCtx<D, RB>& cx, int j, cons
 // PV MFMA; the row sums accumulate in fp32.
 template <int RB>
 __device__ __forceinline__ void softmax_p(const f32x16 (&s)[RB], float sl2, const float (&m_run)[RB],
-                                          float (&l_run)[RB], bf16x8 (&pk)[RB][2]) {
+                                          bf16x8 (&pk)[RB][2]) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const float m_use = (m_run[rb] == -INFINITY) ? 0.f : m_run[rb];
@@ -297,33 +319,40 @@ __device__ __forceinline__ void softmax_p(const f32x16 (&s)[RB], float sl2, cons
         const float p0 = __builtin_amdgcn_exp2f(fmaf(s[rb][8 * sh + 2 * j], sl2, -m_use));
         const float p1 = __builtin_amdgcn_exp2f(fmaf(s[rb][8 * sh + 2 * j + 1], sl2, -m_use));
         u[j] = pack_bf16x2(p0, p1);
-        l_run[rb] += p0 + p1;
       }
       pk[rb][sh] = __builtin_bit_cast(bf16x8, u);
     }
   }
 }
 
-// Raise the running max where the scores of the coming step need it
-// (lazily: only when a row max grows by more than 2^8).
-template <int D, int RB>
-__device__ __forceinline__ void raise_max(const f32x16 (&s)[RB], float sl2, float (&m_run)[RB], float (&l_run)[RB],
-                                          f32x16 (&o)[RB][D / 32]) {
+// row max of S (scaled to log2 units), both halves of the lane pair
+template <int RB>
+__device__ __forceinline__ void row_max(const f32x16 (&s)[RB], float sl2, float (&ms)[RB]) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     float mx = s[rb][0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[rb][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float ms = mx * sl2;
-    if (__any(ms > m_run[rb] + 8.0f)) {
-      const float m_new = fmaxf(m_run[rb], ms);
+    ms[rb] = xor32_max(mx) * sl2;
+  }
+}
+
+// Raise the running max where the scores of the coming step need it
+// (lazily: only when a row max grows by more than 2^8).
+template <int D, int RB>
+__device__ __forceinline__ void raise_max(const float (&ms)[RB], float (&m_run)[RB], f32x16 (&lsum)[RB],
+                                          f32x16 (&o)[RB][D / 32]) {
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    if (__any(ms[rb] > m_run[rb] + 8.0f)) {
+      const float m_new = fmaxf(m_run[rb], ms[rb]);
       const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run[rb] - m_new);
 #pragma unroll
       for (int dg = 0; dg < D / 32; ++dg)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[rb][dg][i] *= alpha;
-      l_run[rb] *= alpha;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) lsum[rb][i] *= alpha;
       m_run[rb] = m_new;
     }
   }
@@ -362,8 +391,8 @@ __global__ void __launch_bounds__(512 / RB, 1) attn_bf16_kernel(AttnParams P) {
   constexpr int BQ = kRows / G;
   constexpr int NKS = D / 16;             // k-steps of QK^T
   constexpr int NDG = D / 32;             // 32-row d blocks of O^T
-  __shared__ BlkDesc lst[kListMax];
-  __shared__ int pos_s[ROPE ? kListMax * kBlock : 1];
+  __shared__ BlkDesc lst[kListMax + kListPad];
+  __shared__ int pos_s[ROPE ? (kListMax + kListPad) * kBlock : 1];
   __shared__ int s_next;
   __shared__ __attribute__((aligned(16))) __bf16 kl[2 * C::KSZ];
   __shared__ __attribute__((aligned(16))) __bf16 vl[2 * C::VSZ];
@@ -444,20 +473,39 @@ __global__ void __launch_bounds__(512 / RB, 1) attn_bf16_kernel(AttnParams P) {
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int i = 0; i < NDG; ++i) o[rb][i] = f32x16{};
-    float m_run[RB], l_run[RB];   // running max of scaled scores (log2 units); half-lane row sums
+    float m_run[RB];       // running max of scaled scores (log2 units)
+    f32x16 lsum[RB];       // running row sums (element 0 of lanes 0..31)
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       m_run[rb] = -INFINITY;
-      l_run[rb] = 0.f;
+      lsum[rb] = f32x16{};
     }
+    // A operand of the row-sum MFMA: row 0 all ones, other rows zero
+    bf16x8 ones;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ones[i] = (__bf16)(l32 == 0 ? 1.0f : 0.0f);
 
     for (int c0 = item.p0; c0 < item.p1; c0 += kListMax) {
       const int n_l = min(kListMax, item.p1 - c0);
       const int nsteps = (n_l + 1) / 2;
       // ---- stage the list piece and the keys' logical positions
-      for (int i = tid; i < n_l; i += NT) lst[i] = blist[c0 + i];
+      for (int i = tid; i < n_l + kListPad; i += NT) {
+        BlkDesc bd;
+        if (i < n_l) {
+          bd = blist[c0 + i];
+        } else {
+          bd.kb = 1 << 26;   // above every query block: never visible
+          bd.phys = -1;
+          bd.span = -1;
+          bd.flags = 0;
+          bd.pos0 = 0;
+          bd.full = 0;
+        }
+        lst[i] = bd;
+      }
       __syncthreads();
       if (ROPE) {
+        for (int i = n_l * kBlock + tid; i < (n_l + kListPad) * kBlock; i += NT) pos_s[i] = 0;
         for (int i = tid; i < n_l * kBlock; i += NT) {
           const BlkDesc bd = lst[i / kBlock];
           int pos = bd.pos0 >= 0 ? bd.pos0 + i % kBlock : lpos[bd.kb * kBlock + i % kBlock];
@@ -490,40 +538,49 @@ __global__ void __launch_bounds__(512 / RB, 1) attn_bf16_kernel(AttnParams P) {
       load_k<D, RB, ROPE>(cx, 1, st);
       store_k<D, RB, ROPE>(cx, 1, st);
       __syncthreads();
-      f32x16 s_cur[RB];
-      qk<D, RB>(cx, 0, qf, s_cur);
-      if (!step_full(cx, 0)) apply_mask(cx, 0, rows, s_cur);
-      raise_max<D, RB>(s_cur, sl2, m_run, l_run, o);
+      f32x16 sa[RB], sb[RB];   // scores of the current / next step (roles alternate)
+      float ms[RB];
+      qk<D, RB>(cx, 0, qf, sa);
+      if (!step_full(cx, 0)) apply_mask(cx, 0, rows, sa);
+      row_max<RB>(sa, sl2, ms);
+      raise_max<D, RB>(ms, m_run, lsum, o);
       load_k<D, RB, ROPE>(cx, 2, st);
       load_v<D, RB>(cx, 1, st);
 
-      for (int s = 0; s < nsteps; ++s) {
-        // ---- one branch-free region: S(s+1) and O += V(s) P(s) on MFMA;
-        // P(s), the rotation of K(s+2) and the stores of K(s+2), V(s+1) on
-        // VALU / LDS; the loads of step s+3 issued at the end
-        f32x16 s_nxt[RB];
+      // One pipeline step s: a branch-free region with S(s+1) and
+      // O += V(s) P(s) on MFMA; P(s), the row max of S(s+1), the rotation of
+      // K(s+2) and the stores of K(s+2), V(s+1) on VALU / LDS; the loads of
+      // step s+3 issued at its end. Then the mask of S(s+1) where needed and
+      // the lazy raise of the running max.
+      auto step = [&](int s, const f32x16 (&s_cur)[RB], f32x16 (&s_nxt)[RB]) {
         qk<D, RB>(cx, (s + 1) & 1, qf, s_nxt);
         bf16x8 pk[RB][2];
-        softmax_p<RB>(s_cur, sl2, m_run, l_run, pk);
-        pv<D, RB>(cx, s & 1, pk, o);
+        softmax_p<RB>(s_cur, sl2, m_run, pk);
+        pv<D, RB>(cx, s & 1, pk, o, lsum, ones);
+        const bool full = step_full(cx, s + 1);
+        row_max<RB>(s_nxt, sl2, ms);
         store_k<D, RB, ROPE>(cx, s & 1, st);
         store_v<D, RB>(cx, (s + 1) & 1, st);
         load_k<D, RB, ROPE>(cx, s + 3, st);
         load_v<D, RB>(cx, s + 2, st);
-        sched_step<RB * NKS, RB * 2 * NDG>();
-        // ---- S(s+1): mask where needed, raise the running max
-        if (!step_full(cx, s + 1)) apply_mask(cx, s + 1, rows, s_nxt);
-        raise_max<D, RB>(s_nxt, sl2, m_run, l_run, o);
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) s_cur[rb] = s_nxt[rb];
+        sched_step<RB * NKS, RB * 2 * NDG + 2 * RB>();
+        if (!full) {
+          apply_mask(cx, s + 1, rows, s_nxt);
+          row_max<RB>(s_nxt, sl2, ms);
+        }
+        raise_max<D, RB>(ms, m_run, lsum, o);
         __syncthreads();
+      };
+      for (int s = 0; s < nsteps; s += 2) {
+        step(s, sa, sb);
+        if (s + 1 < nsteps) step(s + 1, sb, sa);
       }
     }
 
     // ---- epilogue
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const float l_tot = l_run[rb] + __shfl_xor(l_run[rb], 32, 64);
+      const float l_tot = xor32_sum(h == 0 ? lsum[rb][0] : 0.f);
       if (!rows.valid[rb]) continue;
       if (ns == 1) {
         __bf16* op = (__bf16*)P.out + qoff[rb];

@@ -125,35 +125,70 @@ hipError_t launch_rope_table(float* cs, int max_pos, int d, double base, hipStre
 // ---------------------------------------------------------------------------
 // Merge of split tiles: for every split (tile, KV head) group listed by
 // plan_items, combine the pieces' partial results (O, m, l), m in log2 units,
-// as O = sum_s 2^(m_s - m*) O_s / sum_s 2^(m_s - m*) l_s with m* = max_s m_s,
-// summing in piece order. A row is handled by D/4 threads (4 elements each).
+// as O = sum_s 2^(m_s - m*) O_s / sum_s 2^(m_s - m*) l_s with m* = max_s m_s.
+// One work-group unit is a block of RPW rows of one group; a row is handled
+// by D/4 threads (4 elements each). The piece weights are computed lane-
+// parallel (each lane owns pieces lane, lane + D/4, ...) into LDS, then the
+// numerator sums the pieces in piece order with several loads in flight.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int ROWS>
 __global__ void __launch_bounds__(256) merge_kernel(AttnParams P, int G) {
   constexpr int TPR = D / 4;             // threads per row
-  constexpr int RPP = 256 / TPR;         // rows per pass
+  constexpr int RPW = 256 / TPR;         // rows per unit
+  constexpr int NB = ROWS / RPW;         // units per group
+  constexpr int KP = kMaxSplits / TPR;   // pieces per lane in the weight pass
+  constexpr int UNR = 8;                 // pieces loaded together
+  __shared__ float w_s[RPW][kMaxSplits];
   const int ngroups = (int)P.hdr->num_groups;
-  const int bq = ROWS / G;
-  for (int gi = blockIdx.x; gi < ngroups; gi += gridDim.x) {
-    const Group grp = P.groups[gi];
+  const int r_in = threadIdx.x / TPR;
+  const int d4 = threadIdx.x % TPR;
+  for (int u = blockIdx.x; u < ngroups * NB; u += gridDim.x) {
+    const Group grp = P.groups[u / NB];
     const TileDesc td = P.tiles[grp.tile];
-    for (int row = threadIdx.x / TPR; row < ROWS; row += RPP) {
-      const int tok = row / G;
-      if (tok >= td.nq || P.toks[(int64_t)grp.tile * bq + tok].c < 0) continue;
-      const int d4 = threadIdx.x % TPR;
-      float mstar = -INFINITY;
-      for (int s = 0; s < grp.nsplit; ++s)
-        mstar = fmaxf(mstar, P.part_ml[(int64_t)(grp.slot0 + s) * ROWS + row].x);
-      float den = 0.f;
+    const int row = (u % NB) * RPW + r_in;
+    const int tok = row / G;
+    const bool valid = tok < td.nq && P.toks[(int64_t)grp.tile * (ROWS / G) + tok].c >= 0;
+    const int ns = grp.nsplit;
+    const int64_t base = (int64_t)grp.slot0 * ROWS + row;   // row of piece 0; piece s at + s * ROWS
+
+    float m[KP], l[KP];
+    float mstar = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < KP; ++k) {
+      const int s = d4 + TPR * k;
+      const float2 ml = s < ns ? P.part_ml[base + (int64_t)s * ROWS] : make_float2(-INFINITY, 0.f);
+      m[k] = ml.x;
+      l[k] = ml.y;
+      mstar = fmaxf(mstar, ml.x);
+    }
+#pragma unroll
+    for (int o = TPR / 2; o >= 1; o >>= 1) mstar = fmaxf(mstar, __shfl_xor(mstar, o, TPR));
+    float den = 0.f;
+#pragma unroll
+    for (int k = 0; k < KP; ++k) {
+      const int s = d4 + TPR * k;
+      const float w = m[k] == -INFINITY ? 0.f : exp2f(m[k] - mstar);
+      if (s < ns) w_s[r_in][s] = w;
+      den += w * l[k];
+    }
+#pragma unroll
+    for (int o = TPR / 2; o >= 1; o >>= 1) den += __shfl_xor(den, o, TPR);
+    __syncthreads();
+
+    if (valid) {
+      const float* po = P.part_o + base * D + 4 * d4;
       f32x4 num = {0.f, 0.f, 0.f, 0.f};
-      for (int s = 0; s < grp.nsplit; ++s) {
-        const int64_t pr = (int64_t)(grp.slot0 + s) * ROWS + row;
-        const float2 ml = P.part_ml[pr];
-        if (ml.x == -INFINITY) continue;
-        const float wgt = exp2f(ml.x - mstar);
-        den += wgt * ml.y;
-        const f32x4 po = *(const f32x4*)(P.part_o + pr * D + 4 * d4);
-        num += wgt * po;
+      for (int s0 = 0; s0 < ns; s0 += UNR) {
+        f32x4 v[UNR];
+#pragma unroll
+        for (int k = 0; k < UNR; ++k)
+          if (s0 + k < ns) v[k] = *(const f32x4*)(po + (int64_t)(s0 + k) * ROWS * D);
+#pragma unroll
+        for (int k = 0; k < UNR; ++k)
+          if (s0 + k < ns) {
+            const float w = w_s[r_in][s0 + k];
+            if (w != 0.f) num += w * v[k];
+          }
       }
       const float inv = 1.f / den;
       const int64_t qrow = (int64_t)td.row0 + tok;
@@ -168,16 +203,25 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnParams P, int G) {
         *(u32x2*)op = pk;
       }
     }
+    __syncthreads();
   }
 }
 
-hipError_t launch_merge(const AttnParams& p, int D, int dtype, int G, int grid, hipStream_t s) {
+template <typename T, int D, int ROWS>
+static void launch_merge_t(const AttnParams& p, int G, int max_groups, hipStream_t s) {
+  constexpr int NB = ROWS / (256 / (D / 4));
+  const int64_t units = (int64_t)max_groups * NB;
+  const int grid = (int)(units < 4096 ? units : 4096);
+  hipLaunchKernelGGL((merge_kernel<T, D, ROWS>), dim3(grid), dim3(256), 0, s, p, G);
+}
+
+hipError_t launch_merge(const AttnParams& p, int D, int dtype, int G, int max_groups, hipStream_t s) {
   if (dtype == MINIPIC_BF16) {
-    if (D == 128) hipLaunchKernelGGL((merge_kernel<uint16_t, 128, 256>), dim3(grid), dim3(256), 0, s, p, G);
-    else hipLaunchKernelGGL((merge_kernel<uint16_t, 64, 256>), dim3(grid), dim3(256), 0, s, p, G);
+    if (D == 128) launch_merge_t<uint16_t, 128, 256>(p, G, max_groups, s);
+    else launch_merge_t<uint16_t, 64, 256>(p, G, max_groups, s);
   } else {
-    if (D == 128) hipLaunchKernelGGL((merge_kernel<float, 128, 64>), dim3(grid), dim3(256), 0, s, p, G);
-    else hipLaunchKernelGGL((merge_kernel<float, 64, 64>), dim3(grid), dim3(256), 0, s, p, G);
+    if (D == 128) launch_merge_t<float, 128, 64>(p, G, max_groups, s);
+    else launch_merge_t<float, 64, 64>(p, G, max_groups, s);
   }
   return hipGetLastError();
 }

@@ -21,7 +21,7 @@ int attn_f32_blocks_per_cu(int D, int G, bool rope);
 hipError_t launch_write_kv(const void* k, const void* v, const int64_t* slots, int64_t n, int hkv, int D,
                            void* kc, void* vc, int64_t num_blocks, int dtype, hipStream_t s);
 hipError_t launch_rope_table(float* cs, int max_pos, int d, double base, hipStream_t s);
-hipError_t launch_merge(const AttnParams& p, int D, int dtype, int G, int grid, hipStream_t s);
+hipError_t launch_merge(const AttnParams& p, int D, int dtype, int G, int max_groups, hipStream_t s);
 }  // namespace minipic
 
 using namespace minipic;
@@ -246,8 +246,7 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, int64
   e = dtype == MINIPIC_BF16 ? launch_attn_bf16(P, b->head_dim, G, rope, grid, s)
                             : launch_attn_f32(P, b->head_dim, G, rope, grid, s);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
-  const int mgrid = pl.max_groups < 1024 ? pl.max_groups : 1024;
-  e = launch_merge(P, b->head_dim, dtype, G, mgrid, s);
+  e = launch_merge(P, b->head_dim, dtype, G, pl.max_groups, s);
   if (e != hipSuccess) return hip_fail(e, "merge launch");
   return MINIPIC_OK;
 }
