@@ -358,29 +358,18 @@ __device__ __forceinline__ void raise_max(const float (&ms)[RB], float (&m_run)[
   }
 }
 
-// Instruction-scheduling hint for one pipeline step (masks of
-// __builtin_amdgcn_sched_group_barrier: 0x008 MFMA, 0x002 VALU, 0x100 LDS
-// read, 0x200 LDS write, 0x020 global read): the QK^T MFMAs of the next step
-// interleaved with the softmax VALU work of this one, then the PV MFMAs
-// interleaved with the rotation, the LDS stores and the next loads; operand
-// reads from LDS run two MFMAs ahead.
-template <int NQK, int NPV>
-__device__ __forceinline__ void sched_step() {
+// Instruction-scheduling hint for the MFMA part of a step (masks of
+// __builtin_amdgcn_sched_group_barrier: 0x008 MFMA, 0x100 LDS read): the
+// operand reads from LDS run two reads ahead of the MFMAs that use them.
+template <int NRD, int RB>
+__device__ __forceinline__ void sched_mfma() {
   __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-  for (int i = 0; i < NQK; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+  for (int i = 0; i < NRD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);
+    if (i + 2 < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
-#pragma unroll
-  for (int i = 0; i < NPV; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (i + 2 < NPV) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
-    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-  }
+  __builtin_amdgcn_sched_group_barrier(0x008, 2 * RB, 0);
 }
 
 template <int D, int G, bool ROPE, int RB>
@@ -394,6 +383,7 @@ __global__ void __launch_bounds__(512 / RB, 1) attn_bf16_kernel(AttnParams P) {
   __shared__ BlkDesc lst[kListMax + kListPad];
   __shared__ int pos_s[ROPE ? (kListMax + kListPad) * kBlock : 1];
   __shared__ int s_next;
+  __shared__ uint32_t s_qs[kQueues], s_qc[kQueues];
   __shared__ __attribute__((aligned(16))) __bf16 kl[2 * C::KSZ];
   __shared__ __attribute__((aligned(16))) __bf16 vl[2 * C::VSZ];
 
@@ -402,21 +392,31 @@ __global__ void __launch_bounds__(512 / RB, 1) attn_bf16_kernel(AttnParams P) {
   const int w = tid >> 6;
   const int l32 = lane & 31;
   const int h = lane >> 5;
+  // waves w and w + 4 share a SIMD; the first four lead (see the step loop)
+  const bool lead = NT < 512 || w < 4;
 
   const __bf16* kc = (const __bf16*)P.k_cache;
   const __bf16* vc = (const __bf16*)P.v_cache;
   const float sl2 = P.scale_log2;
   const rsrc_t tab = make_rsrc(P.cos_sin, P.max_pos * D * 4);
 
-  int it = next_item(P.hdr, &s_next);
+  if (tid < kQueues) {
+    s_qs[tid] = P.hdr->qstart[tid];
+    s_qc[tid] = P.hdr->qcount[tid];
+  }
+  int q_cur = blockIdx.x % kQueues;   // queue being drained (thread 0)
+  __syncthreads();
+  if (tid == 0) s_next = resolve_ticket(P.hdr, s_qs, s_qc, q_cur, atomicAdd(&P.hdr->next[q_cur], 1u));
+  __syncthreads();
+  int it = __builtin_amdgcn_readfirstlane(s_next);
   while (it >= 0) {
-    if (tid == 0) s_next = claim_item(P.hdr);  // the following item
+    uint32_t ticket = 0;   // claim of the following item, checked when this one ends
+    if (tid == 0) ticket = atomicAdd(&P.hdr->next[q_cur], 1u);
     const Item item = P.items[it];
     const int g = item.gsn & 0xff;
     const int sp = (item.gsn >> 8) & 0xfff;
     const int ns = item.gsn >> 20;
-    const TileDesc td = P.tiles[item.tile];
-    const int32_t* lpos = P.logical_pos + (int64_t)td.r * P.max_blocks * kBlock;
+    const int32_t* lpos = P.logical_pos + (int64_t)item.r * P.max_blocks * kBlock;
     const BlkDesc* blist = P.blist + (int64_t)item.tile * P.max_blocks;
     const int64_t kv_head = (int64_t)g * kBlock * D;   // offset of head g inside a block group
 
@@ -430,13 +430,13 @@ __global__ void __launch_bounds__(512 / RB, 1) attn_bf16_kernel(AttnParams P) {
       row[rb] = 32 * RB * w + 32 * rb + l32;
       const int tok = row[rb] / G;
       const TokDesc tk = P.toks[(int64_t)item.tile * BQ + tok];
-      const bool valid = tok < td.nq && tk.c >= 0;
+      const bool valid = tok < item.nq && tk.c >= 0;
       rows.valid[rb] = valid;
       rows.c[rb] = valid ? tk.c : -1;
       rows.bq[rb] = valid ? (tk.c >> 4) : -1;
       rows.span[rb] = tk.span;
       rows.pdep[rb] = valid && tk.pdep;
-      qoff[rb] = (((int64_t)td.row0 + tok) * P.hq + g * G + row[rb] % G) * D;
+      qoff[rb] = (((int64_t)item.row0 + tok) * P.hq + g * G + row[rb] % G) * D;
       const __bf16* qp = (const __bf16*)P.q + qoff[rb];
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) qf[rb][ks] = valid ? *(const bf16x8*)(qp + 16 * ks + 8 * h) : bf16x8{};
@@ -488,7 +488,8 @@ __global__ void __launch_bounds__(512 / RB, 1) attn_bf16_kernel(AttnParams P) {
     for (int c0 = item.p0; c0 < item.p1; c0 += kListMax) {
       const int n_l = min(kListMax, item.p1 - c0);
       const int nsteps = (n_l + 1) / 2;
-      // ---- stage the list piece and the keys' logical positions
+      // ---- stage the list piece and the keys' logical positions (read from
+      // the list in global memory, so one barrier covers both)
       for (int i = tid; i < n_l + kListPad; i += NT) {
         BlkDesc bd;
         if (i < n_l) {
@@ -503,20 +504,22 @@ __global__ void __launch_bounds__(512 / RB, 1) attn_bf16_kernel(AttnParams P) {
         }
         lst[i] = bd;
       }
-      __syncthreads();
       if (ROPE) {
-        for (int i = n_l * kBlock + tid; i < (n_l + kListPad) * kBlock; i += NT) pos_s[i] = 0;
-        for (int i = tid; i < n_l * kBlock; i += NT) {
-          const BlkDesc bd = lst[i / kBlock];
-          int pos = bd.pos0 >= 0 ? bd.pos0 + i % kBlock : lpos[bd.kb * kBlock + i % kBlock];
-          if (pos < 0 || pos >= P.max_pos) {
-            atomicOr(&P.hdr->err, (uint32_t)MINIPIC_EW_POS);
-            pos = pos < 0 ? 0 : P.max_pos - 1;
+        for (int i = tid; i < (n_l + kListPad) * kBlock; i += NT) {
+          int pos = 0;
+          if (i < n_l * kBlock) {
+            const BlkDesc* bd = blist + c0 + i / kBlock;
+            const int pos0 = bd->pos0;
+            pos = pos0 >= 0 ? pos0 + i % kBlock : lpos[bd->kb * kBlock + i % kBlock];
+            if (pos < 0 || pos >= P.max_pos) {
+              atomicOr(&P.hdr->err, (uint32_t)MINIPIC_EW_POS);
+              pos = pos < 0 ? 0 : P.max_pos - 1;
+            }
           }
           pos_s[i] = pos;
         }
-        __syncthreads();
       }
+      __syncthreads();
 
       StepCtx<D, RB> cx;
       cx.lst = lst;
@@ -529,51 +532,74 @@ __global__ void __launch_bounds__(512 / RB, 1) attn_bf16_kernel(AttnParams P) {
       cx.kl = kl;
       cx.vl = vl;
 
-      // ---- prologue: K(0), V(0), K(1) in LDS; S(0); loads of K(2), V(1) in flight
-      St st;
+      // ---- prologue: K(0), V(0), K(1) in LDS; S(0) (and for the leading
+      // waves P(0)); loads of K(2), V(1) in flight
+      St st, st1;
       load_k<D, RB, ROPE>(cx, 0, st);
       load_v<D, RB>(cx, 0, st);
+      load_k<D, RB, ROPE>(cx, 1, st1);
       store_k<D, RB, ROPE>(cx, 0, st);
       store_v<D, RB>(cx, 0, st);
-      load_k<D, RB, ROPE>(cx, 1, st);
-      store_k<D, RB, ROPE>(cx, 1, st);
-      __syncthreads();
-      f32x16 sa[RB], sb[RB];   // scores of the current / next step (roles alternate)
-      float ms[RB];
-      qk<D, RB>(cx, 0, qf, sa);
-      if (!step_full(cx, 0)) apply_mask(cx, 0, rows, sa);
-      row_max<RB>(sa, sl2, ms);
-      raise_max<D, RB>(ms, m_run, lsum, o);
       load_k<D, RB, ROPE>(cx, 2, st);
       load_v<D, RB>(cx, 1, st);
-
-      // One pipeline step s: a branch-free region with S(s+1) and
-      // O += V(s) P(s) on MFMA; P(s), the row max of S(s+1), the rotation of
-      // K(s+2) and the stores of K(s+2), V(s+1) on VALU / LDS; the loads of
-      // step s+3 issued at its end. Then the mask of S(s+1) where needed and
-      // the lazy raise of the running max.
-      auto step = [&](int s, const f32x16 (&s_cur)[RB], f32x16 (&s_nxt)[RB]) {
-        qk<D, RB>(cx, (s + 1) & 1, qf, s_nxt);
-        bf16x8 pk[RB][2];
-        softmax_p<RB>(s_cur, sl2, m_run, pk);
-        pv<D, RB>(cx, s & 1, pk, o, lsum, ones);
-        const bool full = step_full(cx, s + 1);
-        row_max<RB>(s_nxt, sl2, ms);
+      store_k<D, RB, ROPE>(cx, 1, st1);
+      __syncthreads();
+      f32x16 sc[RB];         // scores S of one step
+      bf16x8 pk[RB][2];      // probabilities P of one step (B operand of the PV MFMA)
+      float ms[RB];
+      // S(j) in sc -> P(j) in pk: mask where the step is not full, raise the
+      // running max where needed, exponentiate
+      auto softmax_step = [&](int j) {
+        const bool full = step_full(cx, j);
+        row_max<RB>(sc, sl2, ms);
+        if (!full) {
+          apply_mask(cx, j, rows, sc);
+          row_max<RB>(sc, sl2, ms);
+        }
+        raise_max<D, RB>(ms, m_run, lsum, o);
+        softmax_p<RB>(sc, sl2, m_run, pk);
+      };
+      // the work-group's share of the tile traffic of step s: rotate and store
+      // K(s+2), store V(s+1), issue the loads of K(s+3), V(s+2)
+      auto tiles = [&](int s) {
         store_k<D, RB, ROPE>(cx, s & 1, st);
         store_v<D, RB>(cx, (s + 1) & 1, st);
         load_k<D, RB, ROPE>(cx, s + 3, st);
         load_v<D, RB>(cx, s + 2, st);
-        sched_step<RB * NKS, RB * 2 * NDG + 2 * RB>();
-        if (!full) {
-          apply_mask(cx, s + 1, rows, s_nxt);
-          row_max<RB>(s_nxt, sl2, ms);
-        }
-        raise_max<D, RB>(ms, m_run, lsum, o);
-        __syncthreads();
       };
-      for (int s = 0; s < nsteps; s += 2) {
-        step(s, sa, sb);
-        if (s + 1 < nsteps) step(s + 1, sb, sa);
+      // S(s+1) = K(s+1) Q^T and O += V(s) P(s), with the row sums of P(s)
+      auto mfma = [&](int s) {
+        qk<D, RB>(cx, (s + 1) & 1, qf, sc);
+        pv<D, RB>(cx, s & 1, pk, o, lsum, ones);
+        sched_mfma<NKS + 2 * NDG, RB>();
+      };
+      qk<D, RB>(cx, 0, qf, sc);
+      if (lead) softmax_step(0);
+      __syncthreads();   // K(0) read by every wave before step 0 reuses its buffer
+
+      // Steps. The two waves sharing a SIMD work in opposite order inside a
+      // step, so that one issues its MFMAs while the other runs its vector
+      // ALU work: a leading wave does the MFMA part of step s first, then the
+      // softmax of S(s+1) and its share of the tile traffic; a trailing wave
+      // does the softmax of S(s) and the tile traffic first, then the MFMAs.
+      // Both read K(s+1), V(s) and write K(s+2), V(s+1) (other buffers) in
+      // step s; one barrier ends each step.
+      if (lead) {
+        for (int s = 0; s < nsteps; ++s) {
+          mfma(s);
+          __builtin_amdgcn_sched_barrier(0);
+          if (s + 1 < nsteps) softmax_step(s + 1);
+          tiles(s);
+          __syncthreads();
+        }
+      } else {
+        for (int s = 0; s < nsteps; ++s) {
+          softmax_step(s);
+          tiles(s);
+          __builtin_amdgcn_sched_barrier(0);
+          mfma(s);
+          __syncthreads();
+        }
       }
     }
 
@@ -596,7 +622,7 @@ __global__ void __launch_bounds__(512 / RB, 1) attn_bf16_kernel(AttnParams P) {
           }
       } else {
         // a piece of a split tile: fp32 partial result to its slot (merged by merge_kernel)
-        const int64_t pr = (int64_t)(td.slot0 + g * ns + sp) * kRows + row[rb];
+        const int64_t pr = (int64_t)(item.slot0 + g * ns + sp) * kRows + row[rb];
         float* po = P.part_o + pr * D;
 #pragma unroll
         for (int dg = 0; dg < NDG; ++dg)
@@ -608,9 +634,10 @@ __global__ void __launch_bounds__(512 / RB, 1) attn_bf16_kernel(AttnParams P) {
         if (h == 0) P.part_ml[pr] = make_float2(m_run[rb], l_tot);
       }
     }
+    if (tid == 0) s_next = resolve_ticket(P.hdr, s_qs, s_qc, q_cur, ticket);
     __syncthreads();
+    // s_next is written again only after the next item's barriers
     it = __builtin_amdgcn_readfirstlane(s_next);
-    __syncthreads();
   }
 }
 

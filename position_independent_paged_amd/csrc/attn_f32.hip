@@ -21,6 +21,7 @@ __global__ void __launch_bounds__(kNTf) attn_f32_kernel(AttnParams P) {
   constexpr int DQ = D / 4;
   __shared__ BlkDesc lst[kListMaxF];
   __shared__ int s_next;
+  __shared__ uint32_t s_qs[kQueues], s_qc[kQueues];
   __shared__ float kt[kBlock][D + 1];
   __shared__ float vt[kBlock][D + 1];
 
@@ -32,23 +33,31 @@ __global__ void __launch_bounds__(kNTf) attn_f32_kernel(AttnParams P) {
   const float sl2 = P.scale_log2;
   const float* kc = (const float*)P.k_cache;
   const float* vc = (const float*)P.v_cache;
-  int it = next_item(P.hdr, &s_next);
+  if (tid < kQueues) {
+    s_qs[tid] = P.hdr->qstart[tid];
+    s_qc[tid] = P.hdr->qcount[tid];
+  }
+  int q_cur = blockIdx.x % kQueues;   // queue being drained (thread 0)
+  __syncthreads();
+  if (tid == 0) s_next = resolve_ticket(P.hdr, s_qs, s_qc, q_cur, atomicAdd(&P.hdr->next[q_cur], 1u));
+  __syncthreads();
+  int it = __builtin_amdgcn_readfirstlane(s_next);
   while (it >= 0) {
-    if (tid == 0) s_next = claim_item(P.hdr);
+    uint32_t ticket = 0;   // claim of the following item, checked when this one ends
+    if (tid == 0) ticket = atomicAdd(&P.hdr->next[q_cur], 1u);
     const Item item = P.items[it];
     const int g = item.gsn & 0xff;
     const int sp = (item.gsn >> 8) & 0xfff;
     const int ns = item.gsn >> 20;
-    const TileDesc td = P.tiles[item.tile];
     const TokDesc tk = P.toks[(int64_t)item.tile * BQ + tok];
-    const bool rvalid = tok < td.nq && tk.c >= 0;
+    const bool rvalid = tok < item.nq && tk.c >= 0;
     const int c_row = rvalid ? tk.c : -1;
     const int bq_row = rvalid ? (c_row >> 4) : -1;
     const int span_row = tk.span;
     const bool pdep_row = rvalid && tk.pdep;
     const int head = g * G + hig;
-    const int64_t qrow = (int64_t)td.row0 + tok;
-    const int32_t* lpos = P.logical_pos + (int64_t)td.r * P.max_blocks * kBlock;
+    const int64_t qrow = (int64_t)item.row0 + tok;
+    const int32_t* lpos = P.logical_pos + (int64_t)item.r * P.max_blocks * kBlock;
     const BlkDesc* blist = P.blist + (int64_t)item.tile * P.max_blocks;
 
     // query slice; with MINIPIC_FLAG_ROTATE_Q the rotate-half partner of
@@ -149,15 +158,16 @@ __global__ void __launch_bounds__(kNTf) attn_f32_kernel(AttnParams P) {
       }
     } else if (rvalid) {
       // a piece of a split tile: fp32 partial result to its slot (merged by merge_kernel)
-      const int64_t pr = (int64_t)(td.slot0 + g * ns + sp) * kRowsF + row;
+      const int64_t pr = (int64_t)(item.slot0 + g * ns + sp) * kRowsF + row;
       float* po = P.part_o + pr * D + qd;
 #pragma unroll
       for (int i = 0; i < DQ; ++i) po[i] = o[i];
       if ((tid & 3) == 0) P.part_ml[pr] = make_float2(m_run, l_run);
     }
+    if (tid == 0) s_next = resolve_ticket(P.hdr, s_qs, s_qc, q_cur, ticket);
     __syncthreads();
+    // s_next is written again only after the next item's barriers
     it = __builtin_amdgcn_readfirstlane(s_next);
-    __syncthreads();
   }
 }
 

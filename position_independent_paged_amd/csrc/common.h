@@ -110,12 +110,18 @@ struct BlkDesc {
   int32_t pad1, pad2;
 };
 
-// One unit of attention work: KV head g of tile `tile`, list entries [p0, p1).
+// One unit of attention work: KV head g of tile `tile`, list entries [p0, p1),
+// with the fields of the tile the attention kernel needs (copied here so an
+// item is one load).
 struct Item {
   int32_t tile;
   int32_t p0;
   int32_t p1;
   uint32_t gsn;    // g | split << 8 | nsplit << 20
+  int32_t r;       // request
+  int32_t row0;    // first packed query row of the tile
+  int32_t nq;      // query tokens in the tile
+  int32_t slot0;   // first partial-result slot of the tile (split tiles only)
 };
 
 __host__ __device__ inline uint32_t pack_gsn(int g, int s, int ns) {
@@ -236,29 +242,21 @@ __device__ __forceinline__ bool block_visible(int kb, int span, int flags, int b
   return kb <= bq && (pdep_row || (flags & MINIPIC_BLK_GLOBAL) || span == span_row);
 }
 
-// Claim the next work item for this work-group (thread 0 only): the own
-// queue first, then the others in turn. Returns an index into the item array,
-// or -1 when every queue is drained.
-__device__ __forceinline__ int claim_item(WsHeader* hdr) {
-  const int home = blockIdx.x % kQueues;
-  for (int k = 0; k < kQueues; ++k) {
-    const int q = (home + k) % kQueues;
-    const uint32_t cnt = hdr->qcount[q];
-    if (__hip_atomic_load(&hdr->next[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= cnt) continue;
-    const uint32_t i = atomicAdd(&hdr->next[q], 1u);
-    if (i < cnt) return (int)(hdr->qstart[q] + i);
+// Work items are claimed with one atomic add on the counter of the queue the
+// work-group is draining, issued when the work-group starts an item; the
+// ticket is checked against the queue's size when that item ends, so the
+// claim's latency hides behind the item's work. A ticket past the end means
+// the queue is drained: the work-group moves on to the next queue (queues
+// never refill), and returns -1 when every queue is drained. `qs`, `qc` hold
+// the queues' first items and sizes (copied to LDS). Thread 0 only.
+__device__ __forceinline__ int resolve_ticket(WsHeader* hdr, const uint32_t* qs, const uint32_t* qc, int& q,
+                                              uint32_t ticket) {
+  for (int k = 0;; ++k) {
+    if (ticket < qc[q]) return (int)(qs[q] + ticket);
+    if (k + 1 >= kQueues) return -1;
+    q = (q + 1) % kQueues;
+    ticket = atomicAdd(&hdr->next[q], 1u);
   }
-  return -1;
-}
-
-// Take the next work item: thread 0 claims it, every thread reads the value
-// through LDS. Contains barriers.
-__device__ __forceinline__ int next_item(WsHeader* hdr, int* slot) {
-  if (threadIdx.x == 0) *slot = claim_item(hdr);
-  __syncthreads();
-  const int v = __builtin_amdgcn_readfirstlane(*slot);  // uniform: lets item fields live in SGPRs
-  __syncthreads();
-  return v;
 }
 
 }  // namespace minipic

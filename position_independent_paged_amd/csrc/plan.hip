@@ -329,7 +329,8 @@ __global__ void __launch_bounds__(kItemThreads) plan_items_kernel(PlanParams P) 
       const int p1 = piece_start(n, ns, s + 1);
       for (int g = 0; g < H; ++g) {
         const int pos = atomicAdd(&bins[bin_index(item_queue(P, t, g, p0), p1 - p0)], 1);
-        P.items[pos] = Item{t, p0, p1, pack_gsn(g, s, ns)};
+        const TileDesc& td = P.tiles[t];
+        P.items[pos] = Item{t, p0, p1, pack_gsn(g, s, ns), td.r, td.row0, td.nq, td.slot0};
       }
     }
   }
