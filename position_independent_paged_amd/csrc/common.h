@@ -47,7 +47,9 @@ typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
 constexpr int kBlock = 16;        // tokens per cache block
 constexpr int kMaxSplits = 64;    // key-list pieces per tile at most
 constexpr int kCostBins = 1024;   // item sort buckets (cost in key blocks, clipped)
-constexpr int kPlanThreads = 256; // plan_tiles work-group size
+constexpr int kPlanThreads = 1024;// plan_tiles work-group size
+constexpr int kPlanBlocksPerThread = 2;  // key blocks per plan_tiles thread and pass
+constexpr int kTileCache = 4096;  // tiles whose list lengths plan_items keeps in LDS
 constexpr int kItemThreads = 1024;// plan_items work-group size
 
 // Work items are kept in kQueues queues, one per XCD of the GPU. The
@@ -85,7 +87,8 @@ struct TileDesc {
   int32_t nlist;   // visible key blocks listed for the tile
   int32_t nsplit;  // pieces the list is cut into
   int32_t slot0;   // first partial-result slot (split tiles only)
-  int32_t pad0, pad1;
+  int32_t item0;   // first of the tile's items, numbered in tile order (plan_items)
+  int32_t pad1;
 };
 
 // One query token of a tile.

@@ -159,37 +159,46 @@ __global__ void __launch_bounds__(kPlanThreads) plan_tiles_kernel(PlanParams P) 
   __syncthreads();
   const int lo = s_lo, hi = s_hi, anyp = s_anyp, phi = s_phi;
 
-  // ---- compacted list: GLOBAL blocks below lo (visible to every row), then
-  // the blocks of [lo, hi] some row sees
+  // ---- compacted list, in block order: the GLOBAL blocks below lo (visible
+  // to every row, below every query block) and the blocks of [lo, hi] some row
+  // sees. A pass covers NT * BPT blocks, each thread owning BPT consecutive
+  // ones, so all loads of a pass are in flight together and one scan places
+  // the visible blocks.
+  constexpr int BPT = kPlanBlocksPerThread;
   BlkDesc* out = P.blist + (int64_t)t * P.max_blocks;
   int n = 0;
-  for (int base = 0; base < lo; base += NT) {
-    const int kb = base + tid;
-    int f = 0;
-    if (kb < lo) f = flg[kb];
-    const bool is = (f & MINIPIC_BLK_GLOBAL) != 0;
-    int tot;
-    const int i = block_excl_scan_pred<NT>(is, tmp, &tot);
-    if (is) out[n + i] = make_blk(P, btab, lpos, L, kb, span[kb], f, 1);  // below every query block
-    n += tot;
-  }
-  for (int base = lo; base <= hi; base += NT) {
-    const int kb = base + tid;
-    bool vis = false, full = true;
-    int f = 0, s = 0;
-    if (kb <= hi) {
-      f = flg[kb];
-      s = span[kb];
-      // visible to some row (vis) / to every row, strictly below its own block (full)
-      for (int e = 0; e < n_e; ++e) {
-        const bool see = kb <= e_bq[e] && (e_pdep[e] || (f & MINIPIC_BLK_GLOBAL) || e_span[e] == s);
-        vis = vis || see;
-        full = full && see && kb < e_bq[e];
+  for (int base = 0; base <= hi; base += NT * BPT) {
+    int f[BPT], s[BPT];
+    bool vis[BPT], full[BPT];
+    int cnt = 0;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      const int kb = base + tid * BPT + j;
+      f[j] = 0;
+      s[j] = 0;
+      vis[j] = false;
+      full[j] = true;
+      if (kb <= hi) {
+        f[j] = flg[kb];
+        s[j] = span[kb];
+        if (kb < lo) {
+          vis[j] = (f[j] & MINIPIC_BLK_GLOBAL) != 0;
+        } else {
+          // visible to some row (vis) / to every row, strictly below its own block (full)
+          for (int e = 0; e < n_e; ++e) {
+            const bool see = kb <= e_bq[e] && (e_pdep[e] || (f[j] & MINIPIC_BLK_GLOBAL) || e_span[e] == s[j]);
+            vis[j] = vis[j] || see;
+            full[j] = full[j] && see && kb < e_bq[e];
+          }
+        }
       }
+      cnt += vis[j] ? 1 : 0;
     }
     int tot;
-    const int i = block_excl_scan_pred<NT>(vis, tmp, &tot);
-    if (vis) out[n + i] = make_blk(P, btab, lpos, L, kb, s, f, full ? 1 : 0);
+    int off = block_excl_scan<NT>(cnt, tmp, &tot);
+#pragma unroll
+    for (int j = 0; j < BPT; ++j)
+      if (vis[j]) out[n + off++] = make_blk(P, btab, lpos, L, base + tid * BPT + j, s[j], f[j], full[j] ? 1 : 0);
     n += tot;
   }
   if (tid == 0) *td = TileDesc{r, row0, nq, n, 0, -1, 0, 0};
@@ -244,15 +253,21 @@ __global__ void __launch_bounds__(kItemThreads) plan_items_kernel(PlanParams P) 
   __shared__ unsigned long long red[NT / 64];
   __shared__ int tmp[NT / 64];
   __shared__ int bins[kQueues * kCostBins];
+  __shared__ int s_nl[kTileCache];
+  __shared__ int s_ioff[kTileCache];
   const int tid = threadIdx.x;
   const int T = P.num_tiles;
   const int H = P.hkv;
+  // list lengths of the tiles, read once (cached in LDS for up to kTileCache tiles)
+  for (int t = tid; t < T && t < kTileCache; t += NT) s_nl[t] = P.tiles[t].nlist;
+  __syncthreads();
+  auto nlist = [&](int t) { return t < kTileCache ? s_nl[t] : P.tiles[t].nlist; };
 
   // ---- piece length: about two pieces of work per persistent work-group,
   // never shorter than min_chunk, and few enough split tiles to fit the
   // partial-result slots
   long long work = 0;
-  for (int t = tid; t < T; t += NT) work += P.tiles[t].nlist;
+  for (int t = tid; t < T; t += NT) work += nlist(t);
   work = block_sum_ll<NT>(work, red) * H;
   const long long per = 2LL * P.num_wg;
   long long cl = (work + per - 1) / per;
@@ -260,7 +275,7 @@ __global__ void __launch_bounds__(kItemThreads) plan_items_kernel(PlanParams P) 
   for (int iter = 0; iter < 40; ++iter) {
     long long slots = 0;
     for (int t = tid; t < T; t += NT) {
-      const int ns = num_pieces(P.tiles[t].nlist, chunk);
+      const int ns = num_pieces(nlist(t), chunk);
       if (ns > 1) slots += (long long)ns * H;
     }
     slots = block_sum_ll<NT>(slots, red);
@@ -268,32 +283,49 @@ __global__ void __launch_bounds__(kItemThreads) plan_items_kernel(PlanParams P) 
     chunk *= 2;
   }
 
-  // ---- pieces and slots per tile
-  int slot_base = 0;
+  // ---- pieces, partial-result slots and first item (in tile order) per tile
+  int slot_base = 0, item_base = 0;
   for (int t0 = 0; t0 < T; t0 += NT) {
     const int t = t0 + tid;
-    const int ns = t < T ? num_pieces(P.tiles[t].nlist, chunk) : 0;
-    int tot;
+    const int ns = t < T ? num_pieces(nlist(t), chunk) : 0;
+    int tot, itot;
     const int off = block_excl_scan<NT>(ns > 1 ? ns * H : 0, tmp, &tot);
+    const int ioff = block_excl_scan<NT>(ns * H, tmp, &itot);
     if (t < T) {
       P.tiles[t].nsplit = ns;
       P.tiles[t].slot0 = ns > 1 ? slot_base + off : -1;
+      P.tiles[t].item0 = item_base + ioff;
+      if (t < kTileCache) s_ioff[t] = item_base + ioff;
     }
     slot_base += tot;
+    item_base += itot;
   }
+  const int n_items = item_base;
+  __syncthreads();
+  auto item0 = [&](int t) { return t < kTileCache ? s_ioff[t] : P.tiles[t].item0; };
+  // Items in tile order are numbered 0 .. n_items-1, (tile, piece, head) with
+  // the head fastest; item i belongs to the last tile whose first item is <= i.
+  auto item_tile = [&](int i) {
+    int lo = 0, hi = T - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (item0(mid) <= i) lo = mid;
+      else hi = mid - 1;
+    }
+    return lo;
+  };
 
   // ---- bucket the items by (queue, length), longest first within a queue
   for (int f = tid; f < kQueues * kCostBins; f += NT) bins[f] = 0;
   __syncthreads();
-  for (int t = tid; t < T; t += NT) {
-    const int n = P.tiles[t].nlist;
+  for (int i = tid; i < n_items; i += NT) {
+    const int t = item_tile(i);
+    const int n = nlist(t);
     const int ns = num_pieces(n, chunk);
-    for (int s = 0; s < ns; ++s) {
-      const int p0 = piece_start(n, ns, s);
-      const int cost = piece_start(n, ns, s + 1) - p0;
-      for (int g = 0; g < H; ++g)
-        atomicAdd(&bins[bin_index(item_queue(P, t, g, p0), cost)], 1);
-    }
+    const int k = i - item0(t);
+    const int p0 = piece_start(n, ns, k / H);
+    const int cost = piece_start(n, ns, k / H + 1) - p0;
+    atomicAdd(&bins[bin_index(item_queue(P, t, k % H, p0), cost)], 1);
   }
   __syncthreads();
   // exclusive scan of the kQueues * kCostBins counters, kFlat per thread
@@ -321,18 +353,17 @@ __global__ void __launch_bounds__(kItemThreads) plan_items_kernel(PlanParams P) 
     P.hdr->next[tid] = 0u;
   }
   __syncthreads();
-  for (int t = tid; t < T; t += NT) {
-    const int n = P.tiles[t].nlist;
+  for (int i = tid; i < n_items; i += NT) {
+    const int t = item_tile(i);
+    const int n = nlist(t);
     const int ns = num_pieces(n, chunk);
-    for (int s = 0; s < ns; ++s) {
-      const int p0 = piece_start(n, ns, s);
-      const int p1 = piece_start(n, ns, s + 1);
-      for (int g = 0; g < H; ++g) {
-        const int pos = atomicAdd(&bins[bin_index(item_queue(P, t, g, p0), p1 - p0)], 1);
-        const TileDesc& td = P.tiles[t];
-        P.items[pos] = Item{t, p0, p1, pack_gsn(g, s, ns), td.r, td.row0, td.nq, td.slot0};
-      }
-    }
+    const int k = i - item0(t);
+    const int s = k / H, g = k % H;
+    const int p0 = piece_start(n, ns, s);
+    const int p1 = piece_start(n, ns, s + 1);
+    const TileDesc td = P.tiles[t];
+    const int pos = atomicAdd(&bins[bin_index(item_queue(P, t, g, p0), p1 - p0)], 1);
+    P.items[pos] = Item{t, p0, p1, pack_gsn(g, s, ns), td.r, td.row0, td.nq, td.slot0};
   }
 
   // ---- split (tile, head) groups for the merge kernel
