@@ -14,13 +14,26 @@ heads, head dim 128, bf16, RoPE base 5e5), one request of 120 SSep spans of
 PDep suffix: 15,872 query tokens over a 31,232-token context.
 
 Prints ONE JSON line. `value` is query tokens per second of the whole step;
-the `roofline` object prices the attention call (its average duration from
-HIP events on the launch stream) against the bf16 MFMA peak using the exact
-count of visible (query, key) pairs: FLOPs = 4 * d * Hq * pairs. The
-`cpu_baseline` object times the float64 CPU oracle on a bounded random sample
-of the same workload's query rows.
+the `roofline` object prices the attention kernel (its average launch
+duration from HIP events the library records around it on the launch stream)
+against the bf16 MFMA peak using the exact count of visible (query, key)
+pairs: FLOPs = 4 * d * Hq * pairs. Its `traffic` is the kernel's HBM bytes per
+launch from rocprofv3 FETCH_SIZE / WRITE_SIZE counters (scaled by what the
+same counters read for a plain copy of known size), read from the record in
+profiles/ while the kernel sources still hash to the values it names, else
+null. The `cpu_baseline` object times the float64 CPU oracle on a bounded
+random sample of the same workload's query rows.
+
+Two helper modes serve the counter record:
+  --calibrate-copy           run a plain device-to-device copy of known size
+                             (profile it with --pmc FETCH_SIZE / WRITE_SIZE)
+  --summarize-counters DIRS  turn rocprofv3 counter CSVs of this script (the
+                             bench runs and the copy runs) into the record
 """
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -34,6 +47,9 @@ METRIC = "prefill attention tokens/s and TFLOP/s (% of MFMA bf16 peak), 1 MI355X
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CUs x 4096 flop/clk x 2.4 GHz
 PEAK_F32_VALU_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ["position_independent_paged_amd/csrc/attn_bf16.hip", "position_independent_paged_amd/csrc/common.h"]
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "attn_bf16_c4_traffic.json")
+COPY_BYTES = 1 << 30
 
 WORKLOADS = {
     "c1": "tiny fp32: 1 request, 2 SSep spans of 32 + 16-token PDep query; Hq 4, Hkv 2, d 64, RoPE base 1e4",
@@ -56,7 +72,83 @@ def parse():
     ap.add_argument("--config", default="c4", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample (0 disables the cpu_baseline leg)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain device copy of known size (counter calibration)")
+    ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
+                                                              "COPY_WRITE_DIR"),
+                    help="write the traffic record from rocprofv3 --pmc output directories")
     return ap.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counter_means(d, counter, name_filter):
+    """Mean per-dispatch value of `counter` over the dispatches whose kernel name contains `name_filter`."""
+    per = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter or name_filter not in r["Kernel_Name"]:
+                continue
+            per[r["Dispatch_Id"]] = per.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit(f"no {counter} rows for kernels matching {name_filter!r} under {d}")
+    return sum(per.values()) / len(per), len(per)
+
+
+def summarize_counters(dirs):
+    fetch_d, write_d, cfetch_d, cwrite_d = dirs
+    kname = "attn_bf16_kernel<128, 4, true"
+    fetch_kib, nf = counter_means(fetch_d, "FETCH_SIZE", kname)
+    write_kib, nw = counter_means(write_d, "WRITE_SIZE", kname)
+    copy_name = "copyBuffer"
+    cfetch_kib, _ = counter_means(cfetch_d, "FETCH_SIZE", copy_name)
+    cwrite_kib, _ = counter_means(cwrite_d, "WRITE_SIZE", copy_name)
+    sf = COPY_BYTES / (cfetch_kib * 1024.0)
+    sw = COPY_BYTES / (cwrite_kib * 1024.0)
+    rec = {
+        "kernel": kname + ", 1>",
+        "workload": "c4",
+        "kernel_sources_sha256": kernel_source_hash(),
+        "fetch_kib_per_dispatch": round(fetch_kib, 1), "fetch_dispatches": nf,
+        "write_kib_per_dispatch": round(write_kib, 1), "write_dispatches": nw,
+        "copy_bytes": COPY_BYTES,
+        "copy_fetch_kib": round(cfetch_kib, 1), "copy_write_kib": round(cwrite_kib, 1),
+        "fetch_scale": round(sf, 4), "write_scale": round(sw, 4),
+        "hbm_bytes_per_launch": int(round((fetch_kib * sf + write_kib * sw) * 1024.0)),
+    }
+    os.makedirs(os.path.dirname(TRAFFIC_RECORD), exist_ok=True)
+    with open(TRAFFIC_RECORD, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the attention kernel from the counter record, if it matches the sources."""
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_sources_sha256") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def calibrate_copy():
+    import torch
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "copies": 5}))
 
 
 def log(*a):
@@ -90,10 +182,14 @@ def cpu_baseline(w, target_s, seed=0):
                 done += len(rows)
         return done, time.perf_counter() - t0
 
-    n0, t0 = run(8)
-    per_row = t0 / max(n0, 1)
-    n = int(max(8, min(int(counts.sum()), target_s / max(per_row, 1e-6))))
-    n, t = run(n)
+    n, t = run(8)
+    # rescale the sample until it takes at least 60% of the target time (the
+    # first rows of a request pay its one-off setup, so small samples mislead)
+    for _ in range(3):
+        if t >= 0.6 * target_s or n >= int(counts.sum()):
+            break
+        n = int(max(8, min(int(counts.sum()), n * target_s / max(t, 1e-6))))
+        n, t = run(n)
     return {"value": n / t, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{n} query rows drawn uniformly from the {int(counts.sum())} of workload {w.name}, "
                       f"float64 numpy oracle, {t:.1f} s"}
@@ -101,6 +197,9 @@ def cpu_baseline(w, target_s, seed=0):
 
 def main():
     a = parse()
+    if a.summarize_counters:
+        summarize_counters(a.summarize_counters)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only: --gpus {a.gpus} / WORLD_SIZE {world} is not supported "
@@ -111,13 +210,16 @@ def main():
     import torch
 
     import workload
-    from position_independent_paged_amd import metrics
+    from position_independent_paged_amd import metrics, minipic_kernel_times, minipic_set_kernel_timing
     from position_independent_paged_amd.staging import DeviceWorkload
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if a.calibrate_copy:
+        calibrate_copy()
+        return
     log(f"[bench] generating {a.config}")
     w = workload.make_config(a.config)
     pairs = metrics.workload_pairs(w)
@@ -164,12 +266,26 @@ def main():
     ms_wkv = timed(dw.write_new, reps)
     log(f"[bench] attn {ms_attn:.4f} ms, prerotated {ms_prerot:.4f} ms, write_kv {ms_wkv:.4f} ms")
 
-    tflops = flops / (ms_attn * 1e-3) / 1e12
+    # ---- the attention kernel alone: HIP events recorded by the library
+    # around each launch, on the launch stream
+    minipic_set_kernel_timing(True)
+    acc = [0.0, 0.0, 0.0]
+    for _ in range(reps):
+        dw.attend()
+        t = minipic_kernel_times()
+        acc = [x + y for x, y in zip(acc, t)]
+    minipic_set_kernel_timing(False)
+    ms_plan, ms_kernel, ms_merge = (x / reps for x in acc)
+    log(f"[bench] kernels: plan {ms_plan:.4f} ms, attention {ms_kernel:.4f} ms, merge {ms_merge:.4f} ms")
+
+    tflops = flops / (ms_kernel * 1e-3) / 1e12
+    call_tflops = flops / (ms_attn * 1e-3) / 1e12
     step_tflops = flops / (ms_step * 1e-3) / 1e12
     value = w.total_q / (ms_step * 1e-3)
     if w.dtype == "bf16":
         roof = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None}
+                "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                "traffic": recorded_traffic() if a.config == "c4" else None}
     else:
         roof = {"bound": "alu", "achieved": round(tflops, 4), "peak": PEAK_F32_VALU_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(tflops / PEAK_F32_VALU_TFLOPS, 6), "traffic": None}
@@ -202,10 +318,14 @@ def main():
             "gflop_per_step": round(flops / 1e9, 3),
         },
         "tflops_step": round(step_tflops, 2),
-        "tflops_attention": round(tflops, 2),
-        "pct_mfma_bf16_peak_attention": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "tflops_attention_call": round(call_tflops, 2),
+        "tflops_attention_kernel": round(tflops, 2),
+        "pct_mfma_bf16_peak_attention_kernel": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "kernels": {
             "prefill_attn_ms": round(ms_attn, 5),
+            "plan_kernels_ms": round(ms_plan, 5),
+            "attention_kernel_ms": round(ms_kernel, 5),
+            "merge_kernel_ms": round(ms_merge, 5),
             "reference_prerotated_ms": round(ms_prerot, 5),
             "rope_overhead_pct": round(100 * (ms_attn / ms_prerot - 1), 2),
             "write_kv_ms": round(ms_wkv, 5),

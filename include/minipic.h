@@ -189,6 +189,21 @@ int minipic_reference_prerotated(const void* q, const void* k_cache, const void*
                                  void* out, void* workspace, size_t workspace_bytes,
                                  uint32_t flags, int32_t dtype, void* stream);
 
+/*
+ * Kernel timing, for measurement (not part of the method). With timing on,
+ * every minipic_prefill_attn / minipic_reference_prerotated call of the
+ * calling host thread also records four HIP events on its stream, around the
+ * planning kernels, the attention kernel and the merge kernel.
+ * minipic_kernel_times waits for the most recent such call of the thread to
+ * finish and writes the three durations in milliseconds to ms[0..2] (plan,
+ * attention, merge). It returns MINIPIC_ERR_INVALID_ARG when timing is off
+ * or no call was timed yet, MINIPIC_ERR_HIP when the events fail. The events
+ * belong to the library (one set per host thread, kept until the process
+ * ends); calls on several streams from one thread overwrite each other's.
+ */
+int minipic_set_kernel_timing(int enable);
+int minipic_kernel_times(float* ms);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,7 @@ MINIPIC_EW_CTX = 8
 EXPORTS = [
     "minipic_version", "minipic_status_string", "minipic_last_error", "minipic_rope_table",
     "minipic_write_kv", "minipic_workspace_size", "minipic_get_launch_info", "minipic_prefill_attn",
-    "minipic_reference_prerotated",
+    "minipic_reference_prerotated", "minipic_set_kernel_timing", "minipic_kernel_times",
 ]
 
 
@@ -82,6 +82,8 @@ def load_library(path: str = LIB_PATH):
             i32, vp]
     lib.minipic_prefill_attn.argtypes = attn
     lib.minipic_reference_prerotated.argtypes = attn
+    lib.minipic_set_kernel_timing.argtypes = [ctypes.c_int]
+    lib.minipic_kernel_times.argtypes = [ctypes.POINTER(ctypes.c_float)]
     for name in EXPORTS[3:]:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -159,3 +161,14 @@ def minipic_reference_prerotated(q, k_cache, v_cache, num_blocks, batch, out, wo
                                  max_pos: int = 0, flags: int = 0, softmax_scale: float = 0.0, stream=None):
     _attn(load_library().minipic_reference_prerotated, q, k_cache, v_cache, num_blocks, batch, cos_sin, max_pos,
           out, workspace, flags, softmax_scale, stream)
+
+
+def minipic_set_kernel_timing(enable: bool):
+    _check(load_library().minipic_set_kernel_timing(1 if enable else 0))
+
+
+def minipic_kernel_times() -> tuple:
+    """(plan, attention, merge) milliseconds of the latest timed attention call of this thread."""
+    ms = (ctypes.c_float * 3)()
+    _check(load_library().minipic_kernel_times(ms))
+    return float(ms[0]), float(ms[1]), float(ms[2])

@@ -157,6 +157,24 @@ int persistent_grid(int dtype, int D, int G, bool rope, int* grid) {
   return 0;
 }
 
+// Optional kernel timing (minipic_set_kernel_timing): events recorded on the
+// call's stream around the three launches of the latest call of this thread.
+struct KernelTimer {
+  bool on = false;
+  bool valid = false;
+  hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
+};
+thread_local KernelTimer g_timer;
+
+hipError_t timer_mark(int i, hipStream_t s) {
+  if (!g_timer.on) return hipSuccess;
+  if (!g_timer.ev[i]) {
+    hipError_t e = hipEventCreate(&g_timer.ev[i]);
+    if (e != hipSuccess) return e;
+  }
+  return hipEventRecord(g_timer.ev[i], s);
+}
+
 int run_attention(const void* q, const void* k_cache, const void* v_cache, int64_t num_blocks,
                   const minipic_batch* b, const float* cos_sin, int32_t max_pos, float softmax_scale,
                   void* out, void* workspace, size_t workspace_bytes, uint32_t flags, int32_t dtype,
@@ -241,13 +259,20 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, int64
   P.scale_log2 = scale * 1.4426950408889634f;
   P.flags = flags;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch_plan(Q, pl.bq, s);
+  g_timer.valid = false;
+  hipError_t e = timer_mark(0, s);
+  if (e == hipSuccess) e = launch_plan(Q, pl.bq, s);
   if (e != hipSuccess) return hip_fail(e, "plan launch");
-  e = dtype == MINIPIC_BF16 ? launch_attn_bf16(P, b->head_dim, G, rope, grid, s)
-                            : launch_attn_f32(P, b->head_dim, G, rope, grid, s);
+  e = timer_mark(1, s);
+  if (e == hipSuccess)
+    e = dtype == MINIPIC_BF16 ? launch_attn_bf16(P, b->head_dim, G, rope, grid, s)
+                              : launch_attn_f32(P, b->head_dim, G, rope, grid, s);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
-  e = launch_merge(P, b->head_dim, dtype, G, pl.max_groups, s);
+  e = timer_mark(2, s);
+  if (e == hipSuccess) e = launch_merge(P, b->head_dim, dtype, G, pl.max_groups, s);
+  if (e == hipSuccess) e = timer_mark(3, s);
   if (e != hipSuccess) return hip_fail(e, "merge launch");
+  g_timer.valid = g_timer.on;
   return MINIPIC_OK;
 }
 
@@ -345,6 +370,21 @@ int minipic_reference_prerotated(const void* q, const void* k_cache, const void*
                                  uint32_t flags, int32_t dtype, void* stream) {
   return run_attention(q, k_cache, v_cache, num_blocks, batch, cos_sin, max_pos, softmax_scale, out, workspace,
                        workspace_bytes, flags, dtype, stream, /*rope=*/false);
+}
+
+int minipic_set_kernel_timing(int enable) {
+  g_timer.on = enable != 0;
+  g_timer.valid = false;
+  return MINIPIC_OK;
+}
+
+int minipic_kernel_times(float* ms) {
+  if (!ms) return fail(MINIPIC_ERR_INVALID_ARG, "ms is NULL");
+  if (!g_timer.on || !g_timer.valid) return fail(MINIPIC_ERR_INVALID_ARG, "no timed call (timing is off or no call yet)");
+  hipError_t e = hipEventSynchronize(g_timer.ev[3]);
+  for (int i = 0; i < 3 && e == hipSuccess; ++i) e = hipEventElapsedTime(&ms[i], g_timer.ev[i], g_timer.ev[i + 1]);
+  if (e != hipSuccess) return hip_fail(e, "kernel timing events");
+  return MINIPIC_OK;
 }
 
 }  // extern "C"
