@@ -46,7 +46,6 @@
 
 namespace minipic {
 
-constexpr int kRows = 256;        // query rows per work item
 constexpr int kKT = 32;           // keys per pipeline step
 constexpr int kListMax = 256;     // list entries staged in LDS per pass
 // Sentinel entries after the last one of a pass (no block: loads return
@@ -72,13 +71,24 @@ __device__ __forceinline__ float xor32_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Work-group shape: RB row blocks per wave, NT threads; each thread stages one
-// K unit of CW rotate-half pairs (a key's elements [CW c, CW c + CW) and
-// [d/2 + CW c, d/2 + CW c + CW)) and VU 16-byte V pieces per step.
+// Work-group shape: NW waves of RB row blocks (32 query rows each), NT
+// threads; each thread stages one K unit of CW rotate-half pairs (a key's
+// elements [CW c, CW c + CW) and [d/2 + CW c, d/2 + CW c + CW)) and VU 16-byte
+// V pieces per step.
+#ifndef MINIPIC_RB
+#define MINIPIC_RB 1
+#endif
+#ifndef MINIPIC_NW
+#define MINIPIC_NW (MINIPIC_RB == 1 ? 8 : 4)
+#endif
+constexpr int kRB = MINIPIC_RB;   // row blocks per wave of the built kernels
+constexpr int kNW = MINIPIC_NW;   // waves per work-group of the built kernels
+
 template <int D, int RB>
 struct Cfg {
-  static constexpr int NT = 512 / RB;
-  static constexpr int CW = RB == 1 ? 4 : 8;
+  static constexpr int NT = 64 * kNW;
+  static constexpr int ROWS = 32 * RB * kNW;     // query rows per work item
+  static constexpr int CW = 4 * D <= NT ? 4 : 8;
   static constexpr int KCH = (D / 2) / CW;       // K units per key
   static constexpr int KUNITS = kKT * KCH;
   static_assert(KUNITS <= NT, "one K unit per thread");
@@ -373,11 +383,11 @@ __device__ __forceinline__ void sched_mfma() {
 }
 
 template <int D, int G, bool ROPE, int RB>
-__global__ void __launch_bounds__(512 / RB, 1) attn_bf16_kernel(AttnParams P) {
+__global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams P) {
   using C = Cfg<D, RB>;
   using St = Stage<D, RB>;
   constexpr int NT = C::NT;
-  constexpr int BQ = kRows / G;
+  constexpr int BQ = C::ROWS / G;
   constexpr int NKS = D / 16;             // k-steps of QK^T
   constexpr int NDG = D / 32;             // 32-row d blocks of O^T
   __shared__ BlkDesc lst[kListMax + kListPad];
@@ -622,7 +632,7 @@ __global__ void __launch_bounds__(512 / RB, 1) attn_bf16_kernel(AttnParams P) {
           }
       } else {
         // a piece of a split tile: fp32 partial result to its slot (merged by merge_kernel)
-        const int64_t pr = (int64_t)(item.slot0 + g * ns + sp) * kRows + row[rb];
+        const int64_t pr = (int64_t)(item.slot0 + g * ns + sp) * C::ROWS + row[rb];
         float* po = P.part_o + pr * D;
 #pragma unroll
         for (int dg = 0; dg < NDG; ++dg)
@@ -641,14 +651,10 @@ __global__ void __launch_bounds__(512 / RB, 1) attn_bf16_kernel(AttnParams P) {
   }
 }
 
-#ifndef MINIPIC_RB
-#define MINIPIC_RB 1
-#endif
-constexpr int kRB = MINIPIC_RB;   // row blocks per wave of the built kernels
 
 template <int D, int G, bool ROPE>
 static hipError_t launch_one(const AttnParams& p, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((attn_bf16_kernel<D, G, ROPE, kRB>), dim3((unsigned)grid), dim3(512 / kRB), 0, s, p);
+  hipLaunchKernelGGL((attn_bf16_kernel<D, G, ROPE, kRB>), dim3((unsigned)grid), dim3(64 * kNW), 0, s, p);
   return hipGetLastError();
 }
 
@@ -663,6 +669,10 @@ static hipError_t launch_g(const AttnParams& p, int G, int grid, hipStream_t s) 
   return hipErrorInvalidValue;
 }
 
+// Query rows per work item and threads per work-group of the built kernels.
+int attn_bf16_rows() { return 32 * kRB * kNW; }
+int attn_bf16_threads() { return 64 * kNW; }
+
 hipError_t launch_attn_bf16(const AttnParams& p, int D, int G, bool rope, int grid, hipStream_t s) {
   if (D == 128) return rope ? launch_g<128, true>(p, G, grid, s) : launch_g<128, false>(p, G, grid, s);
   if (D == 64) return rope ? launch_g<64, true>(p, G, grid, s) : launch_g<64, false>(p, G, grid, s);
@@ -676,7 +686,7 @@ int attn_bf16_blocks_per_cu(int D, int G, bool rope) {
   hipError_t e = hipErrorInvalidValue;
 #define MINIPIC_OCC(DD, GG, RR)                                                                          \
   if (D == DD && G == GG && rope == RR)                                                                 \
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<DD, GG, RR, kRB>, 512 / kRB, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, attn_bf16_kernel<DD, GG, RR, kRB>, 64 * kNW, 0);
   MINIPIC_OCC(128, 1, true) MINIPIC_OCC(128, 2, true) MINIPIC_OCC(128, 4, true) MINIPIC_OCC(128, 8, true)
   MINIPIC_OCC(128, 1, false) MINIPIC_OCC(128, 2, false) MINIPIC_OCC(128, 4, false) MINIPIC_OCC(128, 8, false)
   MINIPIC_OCC(64, 1, true) MINIPIC_OCC(64, 2, true) MINIPIC_OCC(64, 4, true) MINIPIC_OCC(64, 8, true)

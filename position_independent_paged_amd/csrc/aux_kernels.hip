@@ -215,10 +215,17 @@ static void launch_merge_t(const AttnParams& p, int G, int max_groups, hipStream
   hipLaunchKernelGGL((merge_kernel<T, D, ROWS>), dim3(grid), dim3(256), 0, s, p, G);
 }
 
-hipError_t launch_merge(const AttnParams& p, int D, int dtype, int G, int max_groups, hipStream_t s) {
+hipError_t launch_merge(const AttnParams& p, int D, int dtype, int rows, int G, int max_groups, hipStream_t s) {
   if (dtype == MINIPIC_BF16) {
-    if (D == 128) launch_merge_t<uint16_t, 128, 256>(p, G, max_groups, s);
-    else launch_merge_t<uint16_t, 64, 256>(p, G, max_groups, s);
+    if (rows == 256) {
+      if (D == 128) launch_merge_t<uint16_t, 128, 256>(p, G, max_groups, s);
+      else launch_merge_t<uint16_t, 64, 256>(p, G, max_groups, s);
+    } else if (rows == 128) {
+      if (D == 128) launch_merge_t<uint16_t, 128, 128>(p, G, max_groups, s);
+      else launch_merge_t<uint16_t, 64, 128>(p, G, max_groups, s);
+    } else {
+      return hipErrorInvalidValue;
+    }
   } else {
     if (D == 128) launch_merge_t<float, 128, 64>(p, G, max_groups, s);
     else launch_merge_t<float, 64, 64>(p, G, max_groups, s);

@@ -17,11 +17,13 @@ hipError_t launch_plan(const PlanParams& p, int bq, hipStream_t s);
 hipError_t launch_attn_bf16(const AttnParams& p, int D, int G, bool rope, int grid, hipStream_t s);
 hipError_t launch_attn_f32(const AttnParams& p, int D, int G, bool rope, int grid, hipStream_t s);
 int attn_bf16_blocks_per_cu(int D, int G, bool rope);
+int attn_bf16_rows();
+int attn_bf16_threads();
 int attn_f32_blocks_per_cu(int D, int G, bool rope);
 hipError_t launch_write_kv(const void* k, const void* v, const int64_t* slots, int64_t n, int hkv, int D,
                            void* kc, void* vc, int64_t num_blocks, int dtype, hipStream_t s);
 hipError_t launch_rope_table(float* cs, int max_pos, int d, double base, hipStream_t s);
-hipError_t launch_merge(const AttnParams& p, int D, int dtype, int G, int max_groups, hipStream_t s);
+hipError_t launch_merge(const AttnParams& p, int D, int dtype, int rows, int G, int max_groups, hipStream_t s);
 }  // namespace minipic
 
 using namespace minipic;
@@ -97,8 +99,8 @@ int env_int(const char* name, int dflt) {
 void make_plan(const minipic_batch* b, int dtype, Plan* p) {
   const int G = b->num_q_heads / b->num_kv_heads;
   if (dtype == MINIPIC_BF16) {
-    p->rows = 256;
-    p->threads = 512;
+    p->rows = attn_bf16_rows();
+    p->threads = attn_bf16_threads();
   } else {
     p->rows = 64;
     p->threads = 256;
@@ -269,7 +271,7 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, int64
                               : launch_attn_f32(P, b->head_dim, G, rope, grid, s);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   e = timer_mark(2, s);
-  if (e == hipSuccess) e = launch_merge(P, b->head_dim, dtype, G, pl.max_groups, s);
+  if (e == hipSuccess) e = launch_merge(P, b->head_dim, dtype, pl.rows, G, pl.max_groups, s);
   if (e == hipSuccess) e = timer_mark(3, s);
   if (e != hipSuccess) return hip_fail(e, "merge launch");
   g_timer.valid = g_timer.on;
