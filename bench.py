@@ -72,6 +72,8 @@ def parse():
     ap.add_argument("--config", default="c4", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample (0 disables the cpu_baseline leg)")
+    ap.add_argument("--suite", default="c2,c3,c5",
+                    help="other workloads whose attention is timed beside the main one (empty: none)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
@@ -195,6 +197,105 @@ def cpu_baseline(w, target_s, seed=0):
                       f"float64 numpy oracle, {t:.1f} s"}
 
 
+def algorithmic_bytes(w):
+    """Q + out + unique K/V + the cos/sin rows of the distinct positions read (one pass each)."""
+    import numpy as np
+    elem = 2 if w.dtype == "bf16" else 4
+    qo = 2 * int(w.total_q) * w.num_q_heads * w.head_dim * elem
+    blocks, positions = set(), set()
+    for r in range(int(w.num_reqs)):
+        L = int(w.ctx_len[r])
+        nb = (L + w.block_size - 1) // w.block_size
+        blocks.update(int(b) for b in w.block_table[r, :nb])
+        positions.update(int(p) for p in np.unique(w.logical_pos[r, :L]))
+    kv = 2 * len(blocks) * w.block_size * w.num_kv_heads * w.head_dim * elem
+    cs = len(positions) * w.head_dim * 4
+    return qo + kv + cs
+
+
+def kernel_ms(call, reps):
+    """Average (plan, attention, merge) kernel durations of `call` from the library's HIP events."""
+    from position_independent_paged_amd import minipic_kernel_times, minipic_set_kernel_timing
+    minipic_set_kernel_timing(True)
+    acc = [0.0, 0.0, 0.0]
+    try:
+        for _ in range(reps):
+            call()
+            acc = [x + y for x, y in zip(acc, minipic_kernel_times())]
+    finally:
+        minipic_set_kernel_timing(False)
+    return [x / reps for x in acc]
+
+
+def private_copy_prerotated(dw, w, reps):
+    """Attention kernel time of the pre-rotated reference when every request owns private copies of
+    its blocks (a shared span at different positions needs one rotated copy per position)."""
+    import numpy as np
+    import torch
+    from position_independent_paged_amd import minipic_reference_prerotated
+    from position_independent_paged_amd.staging import DeviceBatch
+    R, MB = w.block_table.shape
+    bt = np.full((R, MB), -1, np.int32)
+    src = []
+    for r in range(R):
+        nb = (int(w.ctx_len[r]) + w.block_size - 1) // w.block_size
+        bt[r, :nb] = np.arange(len(src), len(src) + nb, dtype=np.int32)
+        src.extend(int(b) for b in w.block_table[r, :nb])
+    idx = torch.tensor(src, dtype=torch.int64, device=dw.k_cache.device)
+    k_priv = dw.k_cache.index_select(0, idx)
+    v_priv = dw.v_cache.index_select(0, idx)
+    batch = DeviceBatch(q_indptr=w.q_indptr, q_ctx_idx=w.q_ctx_idx, ctx_len=w.ctx_len, block_table=bt,
+                        logical_pos=w.logical_pos, span_id=w.span_id, blk_flags=w.blk_flags,
+                        num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+                        block_size=w.block_size, device=dw.k_cache.device)
+
+    def call():
+        minipic_reference_prerotated(dw.q, k_priv, v_priv, len(src), batch.struct, dw.out, dw.workspace,
+                                     cos_sin=dw.cos_sin, max_pos=dw.max_pos)
+    call()
+    ms = kernel_ms(call, reps)[1]
+    unique = 2 * len(src) * w.block_size * w.num_kv_heads * w.head_dim * (2 if w.dtype == "bf16" else 4)
+    del k_priv, v_priv
+    return ms, unique
+
+
+def suite_entry(name, reps):
+    """Attention kernel of one more workload: time, MFMA and HBM fractions, RoPE overhead."""
+    import torch
+    import workload
+    from position_independent_paged_amd import metrics
+    from position_independent_paged_amd.staging import DeviceWorkload
+    w = workload.make_config(name)
+    dw = DeviceWorkload(w, device="cuda:0")
+    dw.write_new()
+    for _ in range(3):
+        dw.attend()
+        dw.attend_prerotated()
+    torch.cuda.synchronize()
+    if dw.error_word() != 0:
+        raise RuntimeError(f"{name}: kernel error word {dw.error_word():#x}")
+    pairs = metrics.workload_pairs(w)
+    flops = metrics.attention_flops(pairs, w.num_q_heads, w.head_dim)
+    nbytes = algorithmic_bytes(w)
+    plan, attn, merge = kernel_ms(dw.attend, reps)
+    prerot = kernel_ms(dw.attend_prerotated, reps)[1]
+    tf = flops / (attn * 1e-3) / 1e12
+    e = {"workload": WORKLOADS[name], "query_tokens": int(w.total_q), "gflop": round(flops / 1e9, 3),
+         "algorithmic_MB": round(nbytes / 1e6, 1),
+         "attention_kernel_ms": round(attn, 5), "plan_kernels_ms": round(plan, 5), "merge_kernel_ms": round(merge, 5),
+         "tflops_kernel": round(tf, 2), "pct_mfma_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
+         "pct_hbm_peak": round(100 * nbytes / (attn * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+         "prerotated_kernel_ms": round(prerot, 5), "rope_overhead_pct": round(100 * (attn / prerot - 1), 2)}
+    if name == "c3":
+        ms, unique = private_copy_prerotated(dw, w, reps)
+        e["prerotated_private_copies_kernel_ms"] = round(ms, 5)
+        e["prerotated_private_copies_unique_kv_MB"] = round(unique / 1e6, 1)
+        e["rope_overhead_vs_private_copies_pct"] = round(100 * (attn / ms - 1), 2)
+    del dw
+    torch.cuda.empty_cache()
+    return e
+
+
 def main():
     a = parse()
     if a.summarize_counters:
@@ -210,7 +311,7 @@ def main():
     import torch
 
     import workload
-    from position_independent_paged_amd import metrics, minipic_kernel_times, minipic_set_kernel_timing
+    from position_independent_paged_amd import metrics
     from position_independent_paged_amd.staging import DeviceWorkload
 
     if not torch.cuda.is_available():
@@ -268,15 +369,10 @@ def main():
 
     # ---- the attention kernel alone: HIP events recorded by the library
     # around each launch, on the launch stream
-    minipic_set_kernel_timing(True)
-    acc = [0.0, 0.0, 0.0]
-    for _ in range(reps):
-        dw.attend()
-        t = minipic_kernel_times()
-        acc = [x + y for x, y in zip(acc, t)]
-    minipic_set_kernel_timing(False)
-    ms_plan, ms_kernel, ms_merge = (x / reps for x in acc)
-    log(f"[bench] kernels: plan {ms_plan:.4f} ms, attention {ms_kernel:.4f} ms, merge {ms_merge:.4f} ms")
+    ms_plan, ms_kernel, ms_merge = kernel_ms(dw.attend, reps)
+    ms_kernel_prerot = kernel_ms(dw.attend_prerotated, reps)[1]
+    log(f"[bench] kernels: plan {ms_plan:.4f} ms, attention {ms_kernel:.4f} ms, merge {ms_merge:.4f} ms, "
+        f"attention without RoPE {ms_kernel_prerot:.4f} ms")
 
     tflops = flops / (ms_kernel * 1e-3) / 1e12
     call_tflops = flops / (ms_attn * 1e-3) / 1e12
@@ -289,6 +385,13 @@ def main():
     else:
         roof = {"bound": "alu", "achieved": round(tflops, 4), "peak": PEAK_F32_VALU_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(tflops / PEAK_F32_VALU_TFLOPS, 6), "traffic": None}
+
+    suite = {}
+    for name in [n for n in a.suite.split(",") if n and n != a.config]:
+        log(f"[bench] suite: {name}")
+        suite[name] = suite_entry(name, reps)
+        log(f"[bench] suite {name}: {suite[name]['attention_kernel_ms']:.4f} ms, "
+            f"{suite[name]['tflops_kernel']:.1f} TFLOP/s, RoPE +{suite[name]['rope_overhead_pct']:.1f}%")
 
     cpu = None
     if a.cpu_seconds > 0:
@@ -327,13 +430,16 @@ def main():
             "attention_kernel_ms": round(ms_kernel, 5),
             "merge_kernel_ms": round(ms_merge, 5),
             "reference_prerotated_ms": round(ms_prerot, 5),
-            "rope_overhead_pct": round(100 * (ms_attn / ms_prerot - 1), 2),
+            "prerotated_attention_kernel_ms": round(ms_kernel_prerot, 5),
+            "rope_overhead_pct": round(100 * (ms_kernel / ms_kernel_prerot - 1), 2),
+            "pct_hbm_peak_attention_kernel": round(100 * algorithmic_bytes(w) / (ms_kernel * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
             "write_kv_ms": round(ms_wkv, 5),
             "write_kv_GBps": round(kv_bytes / (ms_wkv * 1e-3) / 1e9, 1),
             "plan": info,
         },
         "roofline": roof,
         "cpu_baseline": cpu,
+        "other_workloads": suite,
     }
     print(json.dumps(line), flush=True)
 
