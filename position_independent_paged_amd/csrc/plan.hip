@@ -46,9 +46,8 @@ __device__ __forceinline__ BlkDesc make_blk(const PlanParams& P, const int32_t* 
   return BlkDesc{kb, ph, span, flags, cons ? p[0] : -1, full, 0, 0};
 }
 
-template <int BQ>
-__global__ void __launch_bounds__(kPlanThreads) plan_tiles_kernel(PlanParams P) {
-  constexpr int NT = kPlanThreads;
+template <int BQ, int NT>
+__global__ void __launch_bounds__(NT) plan_tiles_kernel(PlanParams P) {
   static_assert(BQ <= NT, "one query token per thread");
   __shared__ int qblk[BQ];
   __shared__ int e_bq[BQ], e_span[BQ], e_pdep[BQ];
@@ -318,15 +317,35 @@ __global__ void __launch_bounds__(kItemThreads) plan_items_kernel(PlanParams P) 
   // ---- bucket the items by (queue, length), longest first within a queue
   for (int f = tid; f < kQueues * kCostBins; f += NT) bins[f] = 0;
   __syncthreads();
-  for (int i = tid; i < n_items; i += NT) {
-    const int t = item_tile(i);
-    const int n = nlist(t);
-    const int ns = num_pieces(n, chunk);
-    const int k = i - item0(t);
-    const int p0 = piece_start(n, ns, k / H);
-    const int cost = piece_start(n, ns, k / H + 1) - p0;
-    atomicAdd(&bins[bin_index(item_queue(P, t, k % H, p0), cost)], 1);
-  }
+  // Pieces are numbered in tile order (a tile's first piece is item0 / H).
+  // Each thread takes a contiguous run of pieces: the tile of the first is
+  // found by binary search, the following ones by walking forward; a piece's
+  // bounds are computed once for its H items (one per KV head).
+  const int n_pieces = n_items / H;
+  const int per_thread = (n_pieces + NT - 1) / NT;
+  const int q_begin = min(n_pieces, tid * per_thread);
+  const int q_end = min(n_pieces, q_begin + per_thread);
+  auto for_my_pieces = [&](auto&& fn) {
+    if (q_begin >= q_end) return;
+    int t = item_tile(q_begin * H);
+    int first = item0(t) / H, n = nlist(t), ns = num_pieces(n, chunk);
+    for (int q = q_begin; q < q_end; ++q) {
+      while (q >= first + ns) {
+        first += ns;
+        ++t;
+        n = nlist(t);
+        ns = num_pieces(n, chunk);
+      }
+      const int s = q - first;
+      const int p0 = ns == 1 ? 0 : piece_start(n, ns, s);
+      const int p1 = ns == 1 ? n : piece_start(n, ns, s + 1);
+      fn(t, s, ns, p0, p1);
+    }
+  };
+  for_my_pieces([&](int t, int s, int ns, int p0, int p1) {
+    const int cost_bin = bin_index(0, p1 - p0);
+    for (int g = 0; g < H; ++g) atomicAdd(&bins[item_queue(P, t, g, p0) * kCostBins + cost_bin], 1);
+  });
   __syncthreads();
   // exclusive scan of the kQueues * kCostBins counters, kFlat per thread
   constexpr int kFlat = kQueues * kCostBins / NT;
@@ -353,18 +372,19 @@ __global__ void __launch_bounds__(kItemThreads) plan_items_kernel(PlanParams P) 
     P.hdr->next[tid] = 0u;
   }
   __syncthreads();
-  for (int i = tid; i < n_items; i += NT) {
-    const int t = item_tile(i);
-    const int n = nlist(t);
-    const int ns = num_pieces(n, chunk);
-    const int k = i - item0(t);
-    const int s = k / H, g = k % H;
-    const int p0 = piece_start(n, ns, s);
-    const int p1 = piece_start(n, ns, s + 1);
-    const TileDesc td = P.tiles[t];
-    const int pos = atomicAdd(&bins[bin_index(item_queue(P, t, g, p0), p1 - p0)], 1);
-    P.items[pos] = Item{t, p0, p1, pack_gsn(g, s, ns), td.r, td.row0, td.nq, td.slot0};
-  }
+  int t_td = -1;
+  TileDesc td{};
+  for_my_pieces([&](int t, int s, int ns, int p0, int p1) {
+    if (t != t_td) {
+      td = P.tiles[t];
+      t_td = t;
+    }
+    const int cost_bin = bin_index(0, p1 - p0);
+    for (int g = 0; g < H; ++g) {
+      const int pos = atomicAdd(&bins[item_queue(P, t, g, p0) * kCostBins + cost_bin], 1);
+      P.items[pos] = Item{t, p0, p1, pack_gsn(g, s, ns), td.r, td.row0, td.nq, td.slot0};
+    }
+  });
 
   // ---- split (tile, head) groups for the merge kernel
   int group_base = 0;
@@ -386,17 +406,25 @@ __global__ void __launch_bounds__(kItemThreads) plan_items_kernel(PlanParams P) 
   }
 }
 
-hipError_t launch_plan(const PlanParams& p, int bq, hipStream_t s) {
+template <int NT>
+static hipError_t launch_tiles(const PlanParams& p, int bq, hipStream_t s) {
   switch (bq) {
-    case 32: hipLaunchKernelGGL(plan_tiles_kernel<32>, dim3(p.num_tiles), dim3(kPlanThreads), 0, s, p); break;
-    case 64: hipLaunchKernelGGL(plan_tiles_kernel<64>, dim3(p.num_tiles), dim3(kPlanThreads), 0, s, p); break;
-    case 128: hipLaunchKernelGGL(plan_tiles_kernel<128>, dim3(p.num_tiles), dim3(kPlanThreads), 0, s, p); break;
-    case 256: hipLaunchKernelGGL(plan_tiles_kernel<256>, dim3(p.num_tiles), dim3(kPlanThreads), 0, s, p); break;
-    case 8: hipLaunchKernelGGL(plan_tiles_kernel<8>, dim3(p.num_tiles), dim3(kPlanThreads), 0, s, p); break;
-    case 16: hipLaunchKernelGGL(plan_tiles_kernel<16>, dim3(p.num_tiles), dim3(kPlanThreads), 0, s, p); break;
+    case 8: hipLaunchKernelGGL((plan_tiles_kernel<8, NT>), dim3(p.num_tiles), dim3(NT), 0, s, p); break;
+    case 16: hipLaunchKernelGGL((plan_tiles_kernel<16, NT>), dim3(p.num_tiles), dim3(NT), 0, s, p); break;
+    case 32: hipLaunchKernelGGL((plan_tiles_kernel<32, NT>), dim3(p.num_tiles), dim3(NT), 0, s, p); break;
+    case 64: hipLaunchKernelGGL((plan_tiles_kernel<64, NT>), dim3(p.num_tiles), dim3(NT), 0, s, p); break;
+    case 128: hipLaunchKernelGGL((plan_tiles_kernel<128, NT>), dim3(p.num_tiles), dim3(NT), 0, s, p); break;
+    case 256: hipLaunchKernelGGL((plan_tiles_kernel<256, NT>), dim3(p.num_tiles), dim3(NT), 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_plan(const PlanParams& p, int bq, hipStream_t s) {
+  // a request's blocks in one pass where possible; small work-groups for
+  // short contexts (more of them resident per CU)
+  hipError_t e = p.max_blocks <= kPlanBlocksPerThread * 256 ? launch_tiles<256>(p, bq, s)
+                                                              : launch_tiles<kPlanThreads>(p, bq, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(plan_items_kernel, dim3(1), dim3(kItemThreads), 0, s, p);
   return hipGetLastError();
