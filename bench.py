@@ -69,10 +69,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="c4", choices=sorted(WORKLOADS))
+    ap.add_argument("--config", default="c4", choices=sorted(k for k in WORKLOADS if k.startswith("c")))
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample (0 disables the cpu_baseline leg)")
-    ap.add_argument("--suite", default="c2,c3,c5",
+    ap.add_argument("--suite", default="c2,c3,c5,d2,d3,d4,d5",
                     help="other workloads whose attention is timed beside the main one (empty: none)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
@@ -259,8 +259,40 @@ def private_copy_prerotated(dw, w, reps):
     return ms, unique
 
 
+def decode_entry(name, reps):
+    """Decode attention of the decode view of a workload: time against the HBM roofline, RoPE overhead."""
+    import torch
+    import workload
+    from position_independent_paged_amd import metrics
+    from position_independent_paged_amd.staging import DeviceWorkload
+    w = workload.make_config(name)
+    dw = DeviceWorkload(w, device="cuda:0")
+    dw.write_new()
+    for _ in range(3):
+        dw.decode()
+        dw.decode_prerotated()
+    torch.cuda.synchronize()
+    if dw.decode_error_word() != 0:
+        raise RuntimeError(f"{name}: kernel error word {dw.decode_error_word():#x}")
+    nbytes = metrics.decode_bytes(w)
+    _, attn, merge = kernel_ms(dw.decode, reps)
+    prerot = kernel_ms(dw.decode_prerotated, reps)[1]
+    gbs = nbytes / (attn * 1e-3) / 1e9
+    e = {"workload": f"decode step after {name.replace('d', 'c', 1)}: one query row per request (its last "
+                     f"context token)", "requests": int(w.num_reqs), "context_tokens": int(w.ctx_len.sum()),
+         "algorithmic_MB": round(nbytes / 1e6, 2), "decode_kernel_ms": round(attn, 5),
+         "merge_kernel_ms": round(merge, 5), "GBps_kernel": round(gbs, 1),
+         "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2), "prerotated_kernel_ms": round(prerot, 5),
+         "rope_overhead_pct": round(100 * (attn / prerot - 1), 2)}
+    del dw
+    torch.cuda.empty_cache()
+    return e
+
+
 def suite_entry(name, reps):
     """Attention kernel of one more workload: time, MFMA and HBM fractions, RoPE overhead."""
+    if name.startswith("d"):
+        return decode_entry(name, reps)
     import torch
     import workload
     from position_independent_paged_amd import metrics
@@ -390,8 +422,13 @@ def main():
     for name in [n for n in a.suite.split(",") if n and n != a.config]:
         log(f"[bench] suite: {name}")
         suite[name] = suite_entry(name, reps)
-        log(f"[bench] suite {name}: {suite[name]['attention_kernel_ms']:.4f} ms, "
-            f"{suite[name]['tflops_kernel']:.1f} TFLOP/s, RoPE +{suite[name]['rope_overhead_pct']:.1f}%")
+        e = suite[name]
+        if "decode_kernel_ms" in e:
+            log(f"[bench] suite {name}: decode {e['decode_kernel_ms']:.4f} ms, {e['GBps_kernel']:.0f} GB/s, "
+                f"RoPE +{e['rope_overhead_pct']:.1f}%")
+        else:
+            log(f"[bench] suite {name}: {e['attention_kernel_ms']:.4f} ms, {e['tflops_kernel']:.1f} TFLOP/s, "
+                f"RoPE +{e['rope_overhead_pct']:.1f}%")
 
     cpu = None
     if a.cpu_seconds > 0:

@@ -190,10 +190,45 @@ int minipic_reference_prerotated(const void* q, const void* k_cache, const void*
                                  uint32_t flags, int32_t dtype, void* stream);
 
 /*
+ * Decode-phase position-free paged attention: one query row per request
+ * ("MiniPIC ...", §3.2.1 score equation, §3.2.2 rotation of each K tile at
+ * pi(j); visibility rule of §3.1.1 / §3.3.1 as for prefill). Memory bound:
+ * each visible K/V block is read once per KV head.
+ *   q        : [num_reqs][num_q_heads][head_dim] bf16; row r is request r's
+ *              query, already rotated by its own logical position.
+ *   batch    : as for minipic_prefill_attn, with total_q == num_reqs;
+ *              q_ctx_idx[r] is the context index of request r's query (usually
+ *              ctx_len[r] - 1). q_indptr is not read.
+ *   k_cache, v_cache, num_blocks, cos_sin, max_pos, softmax_scale : as for
+ *              minipic_prefill_attn (k_cache holds UNROTATED keys).
+ *   out      : [num_reqs][num_q_heads][head_dim] bf16.
+ *   workspace: minipic_decode_workspace_size() bytes, 256-byte aligned; its
+ *              first uint32_t is the error word, as for prefill.
+ * dtype must be MINIPIC_BF16 (else MINIPIC_ERR_UNSUPPORTED); flags must be 0.
+ * Two kernels run on `stream`: the split attention and the merge of splits.
+ */
+int minipic_decode_workspace_size(const minipic_batch* batch, int32_t dtype, size_t* bytes);
+int minipic_decode_attn(const void* q, const void* k_cache, const void* v_cache, int64_t num_blocks,
+                        const minipic_batch* batch, const float* cos_sin, int32_t max_pos,
+                        float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+                        uint32_t flags, int32_t dtype, void* stream);
+
+/*
+ * Decode without the in-kernel key rotation: k_cache holds keys ALREADY
+ * rotated by their positions (the pre-rotated baseline of "MiniPIC ...",
+ * §3.2.2), for the cost of the rotation in decode.
+ */
+int minipic_decode_prerotated(const void* q, const void* k_cache, const void* v_cache,
+                              int64_t num_blocks, const minipic_batch* batch, float softmax_scale,
+                              void* out, void* workspace, size_t workspace_bytes, uint32_t flags,
+                              int32_t dtype, void* stream);
+
+/*
  * Kernel timing, for measurement (not part of the method). With timing on,
- * every minipic_prefill_attn / minipic_reference_prerotated call of the
- * calling host thread also records four HIP events on its stream, around the
- * planning kernels, the attention kernel and the merge kernel.
+ * every attention call (prefill, decode, and their pre-rotated variants) of
+ * the calling host thread also records four HIP events on its stream, around
+ * the planning kernels (none for decode), the attention kernel and the merge
+ * kernel.
  * minipic_kernel_times waits for the most recent such call of the thread to
  * finish and writes the three durations in milliseconds to ms[0..2] (plan,
  * attention, merge). It returns MINIPIC_ERR_INVALID_ARG when timing is off

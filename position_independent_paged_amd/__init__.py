@@ -8,6 +8,7 @@ ImportError if it has not been built: there is no fallback path.
 from ._binding import (EXPORTS, MINIPIC_BF16, MINIPIC_BLK_GLOBAL, MINIPIC_BLK_PDEP, MINIPIC_EW_BLOCK,
                        MINIPIC_EW_CTX, MINIPIC_EW_POS, MINIPIC_EW_QCTX, MINIPIC_F32, MINIPIC_FLAG_ROTATE_Q,
                        LIB_PATH, MinipicError, load_library, minipic_batch, minipic_get_launch_info,
+                       minipic_decode_attn, minipic_decode_prerotated, minipic_decode_workspace_size,
                        minipic_kernel_times, minipic_prefill_attn, minipic_reference_prerotated,
                        minipic_rope_table, minipic_set_kernel_timing, minipic_version, minipic_workspace_size,
                        minipic_write_kv)
@@ -16,7 +17,8 @@ from ._binding import (EXPORTS, MINIPIC_BF16, MINIPIC_BLK_GLOBAL, MINIPIC_BLK_PD
 __all__ = [
     "EXPORTS", "LIB_PATH", "MinipicError", "load_library", "minipic_batch", "minipic_get_launch_info",
     "minipic_prefill_attn", "minipic_reference_prerotated", "minipic_rope_table", "minipic_version",
-    "minipic_set_kernel_timing", "minipic_kernel_times",
+    "minipic_set_kernel_timing", "minipic_kernel_times", "minipic_decode_workspace_size",
+    "minipic_decode_attn", "minipic_decode_prerotated",
     "minipic_workspace_size", "minipic_write_kv", "MINIPIC_BF16", "MINIPIC_F32", "MINIPIC_BLK_PDEP",
     "MINIPIC_BLK_GLOBAL", "MINIPIC_FLAG_ROTATE_Q", "MINIPIC_EW_BLOCK", "MINIPIC_EW_POS", "MINIPIC_EW_QCTX",
     "MINIPIC_EW_CTX",

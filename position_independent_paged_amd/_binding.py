@@ -29,6 +29,7 @@ EXPORTS = [
     "minipic_version", "minipic_status_string", "minipic_last_error", "minipic_rope_table",
     "minipic_write_kv", "minipic_workspace_size", "minipic_get_launch_info", "minipic_prefill_attn",
     "minipic_reference_prerotated", "minipic_set_kernel_timing", "minipic_kernel_times",
+    "minipic_decode_workspace_size", "minipic_decode_attn", "minipic_decode_prerotated",
 ]
 
 
@@ -82,6 +83,10 @@ def load_library(path: str = LIB_PATH):
             i32, vp]
     lib.minipic_prefill_attn.argtypes = attn
     lib.minipic_reference_prerotated.argtypes = attn
+    lib.minipic_decode_workspace_size.argtypes = [ctypes.POINTER(minipic_batch), i32, ctypes.POINTER(sz)]
+    lib.minipic_decode_attn.argtypes = attn
+    lib.minipic_decode_prerotated.argtypes = [vp, vp, vp, i64, ctypes.POINTER(minipic_batch), ctypes.c_float, vp,
+                                              vp, sz, ctypes.c_uint32, i32, vp]
     lib.minipic_set_kernel_timing.argtypes = [ctypes.c_int]
     lib.minipic_kernel_times.argtypes = [ctypes.POINTER(ctypes.c_float)]
     for name in EXPORTS[3:]:
@@ -172,3 +177,23 @@ def minipic_kernel_times() -> tuple:
     ms = (ctypes.c_float * 3)()
     _check(load_library().minipic_kernel_times(ms))
     return float(ms[0]), float(ms[1]), float(ms[2])
+
+
+def minipic_decode_workspace_size(batch: minipic_batch, dtype_code: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().minipic_decode_workspace_size(ctypes.byref(batch), dtype_code, ctypes.byref(n)))
+    return int(n.value)
+
+
+def minipic_decode_attn(q, k_cache, v_cache, num_blocks, batch, cos_sin, max_pos, out, workspace, *,
+                        flags: int = 0, softmax_scale: float = 0.0, stream=None):
+    _attn(load_library().minipic_decode_attn, q, k_cache, v_cache, num_blocks, batch, cos_sin, max_pos, out,
+          workspace, flags, softmax_scale, stream)
+
+
+def minipic_decode_prerotated(q, k_cache, v_cache, num_blocks, batch, out, workspace, *, flags: int = 0,
+                              softmax_scale: float = 0.0, stream=None):
+    _check(load_library().minipic_decode_prerotated(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), int(num_blocks), ctypes.byref(batch), float(softmax_scale),
+        _ptr(out), _ptr(workspace), int(workspace.numel() * workspace.element_size()), int(flags),
+        _dtype_code(q), _stream(stream)))

@@ -185,6 +185,27 @@ struct AttnParams {
   uint32_t flags;
 };
 
+// Parameters of the decode kernels (one query row per request).
+struct DecodeParams {
+  const void* q;              // [R][Hq][D] bf16, row r = request r's query
+  const void* k_cache;        // [num_blocks][Hkv][16][D]
+  const void* v_cache;        // [num_blocks][Hkv][D][16]
+  void* out;                  // [R][Hq][D]
+  const float* cos_sin;       // [max_pos][D]
+  const int32_t* q_ctx_idx;   // [R] context index of the query
+  const int32_t* ctx_len;     // [R]
+  const int32_t* block_table; // [R][MB]
+  const int32_t* logical_pos; // [R][MB*16]
+  const int32_t* span_id;     // [R][MB]
+  const uint8_t* blk_flags;   // [R][MB]
+  uint32_t* err;              // error word (MINIPIC_EW_* bits)
+  float2* part_ml;            // [R*Hkv*nsplit*G] (m, l)
+  float* part_o;              // [R*Hkv*nsplit*G][D]
+  int64_t num_blocks;
+  int32_t num_reqs, hq, hkv, max_blocks, max_pos, nsplit, split_blocks;
+  float scale_log2;
+};
+
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {

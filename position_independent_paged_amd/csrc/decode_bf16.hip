@@ -1,0 +1,252 @@
+// Decode-phase position-free paged attention (gfx950): one query token per
+// request attends to its request's visible keys, with the key rotation done
+// in-kernel from the unrotated cache ("MiniPIC: Flexible Position-Independent
+// Caching in <100LOC", §3.2.1 score equation and §3.2.2 rotation of each K
+// tile after a cos/sin lookup at pi(j); the visibility rule of §3.1.1 /
+// §3.3.1 as restated in common.h). A generated token belongs to the PDep
+// segment that follows the spans, so it usually sees every earlier key; the
+// kernel applies the general rule from the query's block descriptors.
+//
+// Decode reads every visible K/V block once per KV head for a single query
+// row: it is bound by HBM bandwidth, not by the MFMA. Work split:
+//   * one wave per (request r, KV head g, split s): the split covers a
+//     contiguous run of the request's key blocks (host-chosen length);
+//     invisible blocks are skipped before any K/V load;
+//   * per 16-key block: S^T = K Q^T on v_mfma_f32_16x16x32_bf16 with keys on
+//     M and the G query heads of KV head g on N (columns >= G are zero), after
+//     rotating K in fp32 in registers (lane (key, slice j) holds the rotate-half
+//     pairs d and d + D/2 of its slice); P = exp2(S * scale log2 e - m) with a
+//     lazily raised running max; O^T += V^T P^T on v_mfma_f32_16x16x16bf16_1k,
+//     whose B operand layout is the S accumulator's, and whose A operand is an
+//     8-byte read of the [d][16] V block;
+//   * every wave writes its (O, m, l) partial (m in log2 units); a merge
+//     kernel combines the splits of a (request, query head) in split order.
+#include "common.h"
+
+namespace minipic {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+template <int D, int G, bool ROPE>
+__global__ void __launch_bounds__(64) decode_bf16_kernel(DecodeParams P) {
+  static_assert(G >= 1 && G <= 16, "query heads per KV head fit the 16 MFMA columns");
+  constexpr int NC = D / 32;     // 32-wide d chunks of the QK MFMA
+  constexpr int NH = D / 64;     // chunks in each rotate-half
+  constexpr int NM = D / 16;     // 16-row d blocks of the PV MFMA
+  const int l = threadIdx.x;
+  const int n = l & 15;          // MFMA column: query head n of this KV head / key row of K
+  const int j = l >> 4;          // lane group: d slice 8j..8j+7 of a chunk (QK), keys 4j..4j+3 (S, PV)
+  const int u = blockIdx.x;
+  const int s = u % P.nsplit;
+  const int g = (u / P.nsplit) % P.hkv;
+  const int r = u / (P.nsplit * P.hkv);
+  const int64_t pslot = ((int64_t)(r * P.hkv + g) * P.nsplit + s) * G;
+
+  // ---- the query's context index, block and descriptors (wave-uniform)
+  const int Lmax = P.max_blocks * kBlock;
+  int L = P.ctx_len[r];
+  if (L > Lmax || L < 0) {
+    if (l == 0 && s == 0 && g == 0) atomicOr(P.err, (uint32_t)MINIPIC_EW_CTX);
+    L = L < 0 ? 0 : Lmax;
+  }
+  int c = P.q_ctx_idx[r];
+  if (c < 0 || c >= L) {
+    if (l == 0 && s == 0 && g == 0) atomicOr(P.err, (uint32_t)MINIPIC_EW_QCTX);
+    c = c < 0 ? 0 : L - 1;
+  }
+  const int32_t* span = P.span_id + (int64_t)r * P.max_blocks;
+  const uint8_t* flg = P.blk_flags + (int64_t)r * P.max_blocks;
+  const int32_t* btab = P.block_table + (int64_t)r * P.max_blocks;
+  const int32_t* lpos = P.logical_pos + (int64_t)r * Lmax;
+  const int bq = c >> 4;
+  const int b0 = s * P.split_blocks;
+  const int b1 = min(bq + 1, b0 + P.split_blocks);
+  float m_run = -INFINITY;       // running max of this lane's head (log2 units)
+  float l_run = 0.f;             // this lane's share of the row sum (keys 4j..4j+3 of each block)
+  f32x4 o[NM];
+#pragma unroll
+  for (int i = 0; i < NM; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  if (L > 0 && b0 < b1) {
+    const int span_q = span[bq];
+    const bool pdep_q = (flg[bq] & MINIPIC_BLK_PDEP) != 0;
+    // Q^T operand: lane (n, j) holds d = 32 t + 8 j + [0, 8) of query head g G + n
+    bf16x8 qf[NC];
+    {
+      const bool hv = n < G;
+      const __bf16* qp = (const __bf16*)P.q + ((int64_t)r * P.hq + g * G + (hv ? n : 0)) * D + 8 * j;
+#pragma unroll
+      for (int t = 0; t < NC; ++t) qf[t] = hv ? *(const bf16x8*)(qp + 32 * t) : bf16x8{};
+    }
+    const int64_t group = (int64_t)P.hkv * kBlock * D;
+    const __bf16* kc = (const __bf16*)P.k_cache + (int64_t)g * kBlock * D;
+    const __bf16* vc = (const __bf16*)P.v_cache + (int64_t)g * kBlock * D;
+    const float sl2 = P.scale_log2;
+    for (int b = b0; b < b1; ++b) {
+      const int sb = span[b];
+      const int fb = flg[b];
+      if (!(pdep_q || (fb & MINIPIC_BLK_GLOBAL) || sb == span_q)) continue;   // block invisible to the query
+      int ph = btab[b];
+      if (ph < 0 || (int64_t)ph >= P.num_blocks) {
+        if (l == 0) atomicOr(P.err, (uint32_t)MINIPIC_EW_BLOCK);
+        ph = -1;
+      }
+      // ---- K rows: lane (n, j) = key n of the block, d slices 8 j of every chunk
+      bf16x8 ka[NC];
+      if (ph >= 0) {
+        const __bf16* kr = kc + ph * group + n * D + 8 * j;
+#pragma unroll
+        for (int t = 0; t < NC; ++t) ka[t] = *(const bf16x8*)(kr + 32 * t);
+      } else {
+#pragma unroll
+        for (int t = 0; t < NC; ++t) ka[t] = bf16x8{};
+      }
+      // V^T operand: lane (n, j) = d row 16 mt + n, keys 4 j .. 4 j + 3
+      s16x4 va[NM];
+      if (ph >= 0) {
+        const __bf16* vr = vc + ph * group + n * kBlock + 4 * j;
+#pragma unroll
+        for (int mt = 0; mt < NM; ++mt) va[mt] = *(const s16x4*)(vr + 16 * mt * kBlock);
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < NM; ++mt) va[mt] = s16x4{0, 0, 0, 0};
+      }
+      if (ROPE) {
+        // rotate-half at the key's logical position: element i (first half)
+        // with element i + D/2, in fp32, one rounding to bf16
+        int pos = lpos[b * kBlock + n];
+        if (pos < 0 || pos >= P.max_pos) {
+          atomicOr(P.err, (uint32_t)MINIPIC_EW_POS);
+          pos = pos < 0 ? 0 : P.max_pos - 1;
+        }
+        const float* cs = P.cos_sin + (int64_t)pos * D + 8 * j;
+#pragma unroll
+        for (int t = 0; t < NH; ++t) {
+          const f32x4 c0 = *(const f32x4*)(cs + 32 * t), c1 = *(const f32x4*)(cs + 32 * t + 4);
+          const f32x4 s0 = *(const f32x4*)(cs + D / 2 + 32 * t), s1 = *(const f32x4*)(cs + D / 2 + 32 * t + 4);
+          const float cv[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+          const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+          const u32x4 ua = __builtin_bit_cast(u32x4, ka[t]);
+          const u32x4 ub = __builtin_bit_cast(u32x4, ka[t + NH]);
+          u32x4 ra, rb;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float a0 = bf16_lo(ua[e]), a1 = bf16_hi(ua[e]);
+            const float x0 = bf16_lo(ub[e]), x1 = bf16_hi(ub[e]);
+            const float c_0 = cv[2 * e], c_1 = cv[2 * e + 1], s_0 = sv[2 * e], s_1 = sv[2 * e + 1];
+            ra[e] = pack_bf16x2(a0 * c_0 - x0 * s_0, a1 * c_1 - x1 * s_1);
+            rb[e] = pack_bf16x2(x0 * c_0 + a0 * s_0, x1 * c_1 + a1 * s_1);
+          }
+          ka[t] = __builtin_bit_cast(bf16x8, ra);
+          ka[t + NH] = __builtin_bit_cast(bf16x8, rb);
+        }
+      }
+      // ---- S^T = K Q^T: acc[i] = score of key 4 j + i for head n
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < NC; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[t], qf[t], acc, 0, 0, 0);
+      if (b == bq) {   // causal diagonal: keys after the query
+        const int lim = c - bq * kBlock - 4 * j;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (i > lim) acc[i] = -INFINITY;
+      }
+      // ---- online softmax of head n over this block's 16 keys
+      float mx = fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx *= sl2;
+      if (__any(mx > m_run + 8.0f)) {   // lazy raise (exact: numerator and sum share the stale max)
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
+#pragma unroll
+        for (int mt = 0; mt < NM; ++mt) o[mt] *= alpha;
+        l_run *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = m_run == -INFINITY ? 0.f : m_run;
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(fmaf(acc[i], sl2, -m_use));
+      const uint32_t p01 = pack_bf16x2(p[0], p[1]), p23 = pack_bf16x2(p[2], p[3]);
+      // the row sum of the bf16 values the numerator uses
+      l_run += (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
+      const s16x4 pb = __builtin_bit_cast(s16x4, u32x2{p01, p23});
+      // ---- O^T += V^T P^T
+#pragma unroll
+      for (int mt = 0; mt < NM; ++mt) o[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[mt], pb, o[mt], 0, 0, 0);
+    }
+  }
+  // ---- partial of this split: lane (n, j) holds O^T[d = 16 mt + 4 j + i][head n]
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (n < G) {
+    float* po = P.part_o + (pslot + n) * D + 4 * j;
+#pragma unroll
+    for (int mt = 0; mt < NM; ++mt) *(f32x4*)(po + 16 * mt) = o[mt];
+    if (j == 0) P.part_ml[pslot + n] = make_float2(m_run, l_run);
+  }
+}
+
+// Merge of the splits of one (request, query head): O = sum_s 2^(m_s - m*) O_s /
+// sum_s 2^(m_s - m*) l_s, m* = max_s m_s, summed in split order. One wave per
+// (request, query head); each lane owns D/64 consecutive elements.
+template <int D>
+__global__ void __launch_bounds__(64) decode_merge_kernel(DecodeParams P, int G) {
+  constexpr int E = D / 64;
+  const int l = threadIdx.x;
+  const int h = blockIdx.x % P.hq;
+  const int r = blockIdx.x / P.hq;
+  const int g = h / G, n = h % G;
+  const int64_t base = (int64_t)(r * P.hkv + g) * P.nsplit * G + n;   // split s at base + s G
+  float mstar = -INFINITY;
+  for (int s = l; s < P.nsplit; s += 64) mstar = fmaxf(mstar, P.part_ml[base + (int64_t)s * G].x);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mstar = fmaxf(mstar, __shfl_xor(mstar, o, 64));
+  float num[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) num[e] = 0.f;
+  float den = 0.f;
+  for (int s = 0; s < P.nsplit; ++s) {
+    const int64_t ps = base + (int64_t)s * G;
+    const float2 ml = P.part_ml[ps];
+    if (ml.x == -INFINITY) continue;   // split without visible keys
+    const float w = exp2f(ml.x - mstar);
+    den += w * ml.y;
+#pragma unroll
+    for (int e = 0; e < E; ++e) num[e] += w * P.part_o[ps * D + E * l + e];
+  }
+  const float inv = 1.f / den;
+  __bf16* op = (__bf16*)P.out + ((int64_t)r * P.hq + h) * D + E * l;
+#pragma unroll
+  for (int e = 0; e < E; ++e) op[e] = (__bf16)(num[e] * inv);
+}
+
+template <int D, bool ROPE>
+static hipError_t launch_dec_g(const DecodeParams& p, int G, hipStream_t s) {
+  const dim3 grid((unsigned)((int64_t)p.num_reqs * p.hkv * p.nsplit));
+  switch (G) {
+    case 1: hipLaunchKernelGGL((decode_bf16_kernel<D, 1, ROPE>), grid, dim3(64), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((decode_bf16_kernel<D, 2, ROPE>), grid, dim3(64), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((decode_bf16_kernel<D, 4, ROPE>), grid, dim3(64), 0, s, p); break;
+    case 8: hipLaunchKernelGGL((decode_bf16_kernel<D, 8, ROPE>), grid, dim3(64), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_bf16(const DecodeParams& p, int D, int G, bool rope, hipStream_t s) {
+  if (D == 128) return rope ? launch_dec_g<128, true>(p, G, s) : launch_dec_g<128, false>(p, G, s);
+  if (D == 64) return rope ? launch_dec_g<64, true>(p, G, s) : launch_dec_g<64, false>(p, G, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_merge(const DecodeParams& p, int D, int G, hipStream_t s) {
+  const dim3 grid((unsigned)((int64_t)p.num_reqs * p.hq));
+  if (D == 128) hipLaunchKernelGGL((decode_merge_kernel<128>), grid, dim3(64), 0, s, p, G);
+  else if (D == 64) hipLaunchKernelGGL((decode_merge_kernel<64>), grid, dim3(64), 0, s, p, G);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace minipic

@@ -24,6 +24,8 @@ hipError_t launch_write_kv(const void* k, const void* v, const int64_t* slots, i
                            void* kc, void* vc, int64_t num_blocks, int dtype, hipStream_t s);
 hipError_t launch_rope_table(float* cs, int max_pos, int d, double base, hipStream_t s);
 hipError_t launch_merge(const AttnParams& p, int D, int dtype, int rows, int G, int max_groups, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeParams& p, int D, int G, bool rope, hipStream_t s);
+hipError_t launch_decode_merge(const DecodeParams& p, int D, int G, hipStream_t s);
 }  // namespace minipic
 
 using namespace minipic;
@@ -87,6 +89,124 @@ int check_batch(const minipic_batch* b, int dtype) {
   }
   if (b->total_q > (int64_t)INT32_MAX) return fail(MINIPIC_ERR_INVALID_ARG, "total_q too large");
   if ((uintptr_t)b->logical_pos % 16) return fail(MINIPIC_ERR_INVALID_ARG, "logical_pos must be 16-byte aligned");
+  return MINIPIC_OK;
+}
+
+// Optional kernel timing (minipic_set_kernel_timing): events recorded on the
+// call's stream around the three launches of the latest call of this thread.
+struct KernelTimer {
+  bool on = false;
+  bool valid = false;
+  hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
+};
+thread_local KernelTimer g_timer;
+
+hipError_t timer_mark(int i, hipStream_t s) {
+  if (!g_timer.on) return hipSuccess;
+  if (!g_timer.ev[i]) {
+    hipError_t e = hipEventCreate(&g_timer.ev[i]);
+    if (e != hipSuccess) return e;
+  }
+  return hipEventRecord(g_timer.ev[i], s);
+}
+
+// Decode plan (host scalars only): key splits per (request, KV head) so that
+// about kDecodeWaves waves cover the batch, every split at least two blocks.
+constexpr int64_t kDecodeWaves = 4096;
+struct DecodePlan {
+  int split_blocks, nsplit;
+  size_t off_ml, off_o, bytes;
+};
+
+void make_decode_plan(const minipic_batch* b, DecodePlan* p) {
+  const int64_t MB = b->max_blocks_per_req;
+  const int64_t per = (int64_t)b->num_reqs * b->num_kv_heads * MB;
+  int64_t sb = (per + kDecodeWaves - 1) / kDecodeWaves;
+  if (sb < 2) sb = 2;
+  p->split_blocks = (int)sb;
+  p->nsplit = (int)((MB + sb - 1) / sb);
+  const int64_t parts = (int64_t)b->num_reqs * b->num_q_heads * p->nsplit;   // (request, KV head, split, head in group)
+  size_t off = kAlign;   // header: the error word
+  p->off_ml = off;
+  off = align_up(off + sizeof(float) * 2 * (size_t)parts);
+  p->off_o = off;
+  off = align_up(off + sizeof(float) * (size_t)parts * b->head_dim);
+  p->bytes = off;
+}
+
+int check_decode(const minipic_batch* b, int dtype) {
+  int st = check_batch(b, dtype);
+  if (st) return st;
+  if (dtype != MINIPIC_BF16) return fail(MINIPIC_ERR_UNSUPPORTED, "decode attention supports MINIPIC_BF16 only");
+  if (b->total_q != b->num_reqs)
+    return fail(MINIPIC_ERR_INVALID_ARG, "decode takes one query row per request (total_q %lld, num_reqs %d)",
+                (long long)b->total_q, b->num_reqs);
+  return MINIPIC_OK;
+}
+
+int run_decode(const void* q, const void* k_cache, const void* v_cache, int64_t num_blocks,
+               const minipic_batch* b, const float* cos_sin, int32_t max_pos, float softmax_scale, void* out,
+               void* workspace, size_t workspace_bytes, uint32_t flags, int32_t dtype, void* stream, bool rope) {
+  int st = check_decode(b, dtype);
+  if (st) return st;
+  if (flags) return fail(MINIPIC_ERR_INVALID_ARG, "decode takes no flags (q arrives rotated), got 0x%x", flags);
+  if (num_blocks < 0) return fail(MINIPIC_ERR_INVALID_ARG, "num_blocks < 0");
+  if (rope) {
+    if (!cos_sin) return fail(MINIPIC_ERR_INVALID_ARG, "cos_sin is NULL");
+    if (max_pos <= 0) return fail(MINIPIC_ERR_INVALID_ARG, "max_pos must be > 0");
+  }
+  if (b->num_reqs == 0) return MINIPIC_OK;
+  if (!q || !out) return fail(MINIPIC_ERR_INVALID_ARG, "q or out is NULL");
+  if (!k_cache || !v_cache) return fail(MINIPIC_ERR_INVALID_ARG, "k_cache or v_cache is NULL");
+  if (num_blocks == 0) return fail(MINIPIC_ERR_INVALID_ARG, "num_blocks is 0");
+  if (!(softmax_scale == softmax_scale) || std::isinf(softmax_scale))
+    return fail(MINIPIC_ERR_INVALID_ARG, "softmax_scale is not finite");
+  DecodePlan pl;
+  make_decode_plan(b, &pl);
+  if (!workspace) return fail(MINIPIC_ERR_INVALID_ARG, "workspace is NULL");
+  if ((uintptr_t)workspace % kAlign) return fail(MINIPIC_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (workspace_bytes < pl.bytes)
+    return fail(MINIPIC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, pl.bytes);
+  if ((int64_t)b->num_reqs * b->num_kv_heads * pl.nsplit > (int64_t)INT32_MAX / 2)
+    return fail(MINIPIC_ERR_INVALID_ARG, "batch too large for one launch");
+  char* ws = (char*)workspace;
+  DecodeParams P{};
+  P.q = q;
+  P.k_cache = k_cache;
+  P.v_cache = v_cache;
+  P.out = out;
+  P.cos_sin = cos_sin;
+  P.q_ctx_idx = b->q_ctx_idx;
+  P.ctx_len = b->ctx_len;
+  P.block_table = b->block_table;
+  P.logical_pos = b->logical_pos;
+  P.span_id = b->span_id;
+  P.blk_flags = b->blk_flags;
+  P.err = (uint32_t*)ws;
+  P.part_ml = (float2*)(ws + pl.off_ml);
+  P.part_o = (float*)(ws + pl.off_o);
+  P.num_blocks = num_blocks;
+  P.num_reqs = b->num_reqs;
+  P.hq = b->num_q_heads;
+  P.hkv = b->num_kv_heads;
+  P.max_blocks = b->max_blocks_per_req;
+  P.max_pos = rope ? max_pos : 1;
+  P.nsplit = pl.nsplit;
+  P.split_blocks = pl.split_blocks;
+  const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)b->head_dim);
+  P.scale_log2 = scale * 1.4426950408889634f;
+  const int G = b->num_q_heads / b->num_kv_heads;
+  hipStream_t s = (hipStream_t)stream;
+  g_timer.valid = false;
+  hipError_t e = timer_mark(0, s);
+  if (e == hipSuccess) e = timer_mark(1, s);
+  if (e == hipSuccess) e = launch_decode_bf16(P, b->head_dim, G, rope, s);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  e = timer_mark(2, s);
+  if (e == hipSuccess) e = launch_decode_merge(P, b->head_dim, G, s);
+  if (e == hipSuccess) e = timer_mark(3, s);
+  if (e != hipSuccess) return hip_fail(e, "decode merge launch");
+  g_timer.valid = g_timer.on;
   return MINIPIC_OK;
 }
 
@@ -157,24 +277,6 @@ int persistent_grid(int dtype, int D, int G, bool rope, int* grid) {
   if (c) *c = g;
   *grid = g;
   return 0;
-}
-
-// Optional kernel timing (minipic_set_kernel_timing): events recorded on the
-// call's stream around the three launches of the latest call of this thread.
-struct KernelTimer {
-  bool on = false;
-  bool valid = false;
-  hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
-};
-thread_local KernelTimer g_timer;
-
-hipError_t timer_mark(int i, hipStream_t s) {
-  if (!g_timer.on) return hipSuccess;
-  if (!g_timer.ev[i]) {
-    hipError_t e = hipEventCreate(&g_timer.ev[i]);
-    if (e != hipSuccess) return e;
-  }
-  return hipEventRecord(g_timer.ev[i], s);
 }
 
 int run_attention(const void* q, const void* k_cache, const void* v_cache, int64_t num_blocks,
@@ -372,6 +474,31 @@ int minipic_reference_prerotated(const void* q, const void* k_cache, const void*
                                  uint32_t flags, int32_t dtype, void* stream) {
   return run_attention(q, k_cache, v_cache, num_blocks, batch, cos_sin, max_pos, softmax_scale, out, workspace,
                        workspace_bytes, flags, dtype, stream, /*rope=*/false);
+}
+
+int minipic_decode_workspace_size(const minipic_batch* batch, int32_t dtype, size_t* bytes) {
+  if (!bytes) return fail(MINIPIC_ERR_INVALID_ARG, "bytes is NULL");
+  int st = check_decode(batch, dtype);
+  if (st) return st;
+  DecodePlan pl;
+  make_decode_plan(batch, &pl);
+  *bytes = pl.bytes;
+  return MINIPIC_OK;
+}
+
+int minipic_decode_attn(const void* q, const void* k_cache, const void* v_cache, int64_t num_blocks,
+                        const minipic_batch* batch, const float* cos_sin, int32_t max_pos, float softmax_scale,
+                        void* out, void* workspace, size_t workspace_bytes, uint32_t flags, int32_t dtype,
+                        void* stream) {
+  return run_decode(q, k_cache, v_cache, num_blocks, batch, cos_sin, max_pos, softmax_scale, out, workspace,
+                    workspace_bytes, flags, dtype, stream, /*rope=*/true);
+}
+
+int minipic_decode_prerotated(const void* q, const void* k_cache, const void* v_cache, int64_t num_blocks,
+                              const minipic_batch* batch, float softmax_scale, void* out, void* workspace,
+                              size_t workspace_bytes, uint32_t flags, int32_t dtype, void* stream) {
+  return run_decode(q, k_cache, v_cache, num_blocks, batch, nullptr, 0, softmax_scale, out, workspace,
+                    workspace_bytes, flags, dtype, stream, /*rope=*/false);
 }
 
 int minipic_set_kernel_timing(int enable) {

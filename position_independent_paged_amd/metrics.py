@@ -49,3 +49,21 @@ def attention_flops(pairs: int, num_q_heads: int, head_dim: int) -> int:
 
 def workload_pairs(w) -> int:
     return visible_pairs(w.q_indptr, w.q_ctx_idx, w.ctx_len, w.span_id, w.blk_flags, w.block_size)
+
+
+def decode_bytes(w) -> int:
+    """Algorithmic HBM bytes of one decode call (one query row per request):
+    q and out rows, K and V of every key block the query sees (once per KV
+    head), and one cos/sin row per visible key position."""
+    elem = 2 if w.dtype == "bf16" else 4
+    bs = w.block_size
+    total = 2 * int(w.total_q) * w.num_q_heads * w.head_dim * elem
+    for r in range(int(w.num_reqs)):
+        for c in np.asarray(w.q_ctx_idx[w.q_indptr[r]:w.q_indptr[r + 1]], np.int64):
+            bq = int(c) // bs
+            sp = np.asarray(w.span_id[r][:bq + 1])
+            fl = np.asarray(w.blk_flags[r][:bq + 1]).astype(np.int64)
+            vis = np.ones(bq + 1, bool) if fl[bq] & PDEP else ((fl & GLOBAL) != 0) | (sp == sp[bq])
+            keys = int(vis.sum()) * bs - (bs - 1 - int(c) % bs)    # the query's own block up to itself
+            total += keys * (2 * w.num_kv_heads * w.head_dim * elem + w.head_dim * 4)
+    return total

@@ -15,7 +15,8 @@ import torch
 
 from ._binding import (MINIPIC_BF16, MINIPIC_F32, minipic_batch, minipic_get_launch_info,
                        minipic_prefill_attn, minipic_reference_prerotated, minipic_rope_table,
-                       minipic_workspace_size, minipic_write_kv)
+                       minipic_workspace_size, minipic_write_kv, minipic_decode_attn,
+                       minipic_decode_prerotated, minipic_decode_workspace_size)
 
 
 def _dev(a, device, dtype=None):
@@ -119,6 +120,26 @@ class DeviceWorkload:
                                      self.v_cache, self.num_blocks, self.batch.struct,
                                      self.out if out is None else out, self.workspace, cos_sin=self.cos_sin,
                                      max_pos=self.max_pos, flags=self.flags if flags is None else flags)
+
+    def _decode_ws(self):
+        if getattr(self, "decode_workspace", None) is None:
+            n = minipic_decode_workspace_size(self.batch.struct, self.dtype_code)
+            self.decode_workspace = torch.zeros(max(n, 256), dtype=torch.uint8, device=self.device)
+        return self.decode_workspace
+
+    def decode(self, out=None, q=None):
+        """Decode attention: the batch must hold one query row per request."""
+        minipic_decode_attn(self.q if q is None else q, self.k_cache, self.v_cache, self.num_blocks,
+                            self.batch.struct, self.cos_sin, self.max_pos, self.out if out is None else out,
+                            self._decode_ws())
+
+    def decode_prerotated(self, out=None, k_cache=None, q=None):
+        minipic_decode_prerotated(self.q if q is None else q, self.k_cache if k_cache is None else k_cache,
+                                  self.v_cache, self.num_blocks, self.batch.struct,
+                                  self.out if out is None else out, self._decode_ws())
+
+    def decode_error_word(self) -> int:
+        return int(self._decode_ws()[:4].view(torch.int32).item())
 
     def step(self):
         """One pass of the hot path: write this step's K~/V, then attend."""

@@ -94,6 +94,43 @@ def test_empty_batch_is_a_no_op():
     assert _attn(_batch(num_reqs=0, total_q=0, max_q_len=0)) == 0
 
 
+def _decode(lib, b, dtype=pip.MINIPIC_BF16, flags=0, ws=1 << 20, cos=256, max_pos=64):
+    return lib.minipic_decode_attn(256, 256, 256, 10, ctypes.byref(b), cos, max_pos, 0.0, 256, 256, ws,
+                                   flags, dtype, None)
+
+
+def test_decode_validation():
+    """Every argument check runs before the first HIP call (testable without a GPU)."""
+    lib = pip.load_library()
+    one = dict(total_q=2, max_q_len=1, num_reqs=2)      # one query row per request
+    assert _decode(lib, _batch(**one), dtype=pip.MINIPIC_F32) == -2
+    assert _decode(lib, _batch(total_q=8, max_q_len=4, num_reqs=2)) == -1   # not one row per request
+    assert b"one query row" in lib.minipic_last_error()
+    assert _decode(lib, _batch(**one), flags=pip.MINIPIC_FLAG_ROTATE_Q) == -1
+    assert _decode(lib, _batch(**one), cos=0) == -1
+    assert _decode(lib, _batch(**one), max_pos=0) == -1
+    assert _decode(lib, _batch(**one), ws=16) == -3
+    assert _decode(lib, _batch(**one, head_dim=96)) == -2
+    # the pre-rotated variant needs no table; an empty batch is a no-op
+    b = _batch(**one)
+    assert lib.minipic_decode_prerotated(256, 256, 256, 10, ctypes.byref(b), 0.0, 256, 256, 16, 0,
+                                         pip.MINIPIC_BF16, None) == -3
+    assert _decode(lib, _batch(num_reqs=0, total_q=0, max_q_len=0)) == 0
+
+
+def test_decode_workspace_grows_with_the_batch():
+    lib = pip.load_library()
+    sizes = []
+    for R, mb in [(1, 4), (1, 64), (4, 64), (64, 256)]:
+        b = _batch(num_reqs=R, total_q=R, max_q_len=1, max_blocks_per_req=mb, max_ctx_len=16 * mb)
+        n = ctypes.c_size_t(0)
+        assert lib.minipic_decode_workspace_size(ctypes.byref(b), pip.MINIPIC_BF16, ctypes.byref(n)) == 0
+        sizes.append(n.value)
+    assert sizes == sorted(sizes) and sizes[0] >= 256
+    # partial results of every (request, query head, split): at least Hq * (d + 2) floats per request
+    assert sizes[-1] >= 64 * 8 * (128 + 2) * 4
+
+
 def test_write_kv_validation():
     lib = pip.load_library()
     wk = lambda **kw: lib.minipic_write_kv(*[kw.get(k, v) for k, v in [

@@ -371,8 +371,42 @@ CONFIGS = {
 }
 
 
+def decode_view(w: Workload, seed: int = 0) -> Workload:
+    """The decode step after a prefill batch: every request's last context
+    token is its one query row.
+
+    The query vector is the prefill batch's row for that token when the token
+    was queried there, else a seeded N(0,1) draw. The token's K/V are the
+    step's new entries; every other token is cached at set-up.
+    """
+    R = w.num_reqs
+    q_ctx = (w.ctx_len.astype(np.int64) - 1).astype(np.int32)
+    rows = np.full(R, -1, np.int64)
+    for r in range(R):
+        q0, q1 = int(w.q_indptr[r]), int(w.q_indptr[r + 1])
+        hit = np.nonzero(w.q_ctx_idx[q0:q1] == q_ctx[r])[0]
+        if len(hit):
+            rows[r] = q0 + int(hit[0])
+    q = np.empty((R,) + w.q.shape[1:], w.q.dtype)
+    have = rows >= 0
+    q[have] = w.q[rows[have]]
+    if (~have).any():
+        rng = np.random.Generator(np.random.PCG64(seed))
+        x = rng.standard_normal((int((~have).sum()),) + w.q.shape[1:], dtype=np.float32)
+        q[~have] = f32_to_bf16_bits(x) if w.dtype == "bf16" else x
+    new_tok = np.array([w.tok_of_ctx[r][q_ctx[r]] for r in range(R)], np.int64)
+    written = np.zeros(len(w.tok_slot), bool)
+    written[new_tok] = True
+    return dataclasses.replace(w, name=w.name.replace("c", "d", 1) if w.name.startswith("c") else w.name + "_decode",
+                               q_indptr=np.arange(R + 1, dtype=np.int32), q_ctx_idx=q_ctx, q=q,
+                               new_tok=new_tok, setup_tok=np.nonzero(~written)[0])
+
+
 def make_config(name: str, seed: Optional[int] = None) -> Workload:
-    """Benchmark workloads c1..c5 and reduced variants used by parity tests."""
+    """Benchmark workloads c1..c5, reduced variants used by parity tests, and
+    d2..d5 (and d*_small): the decode step after the prefill of c2..c5."""
+    if name.startswith("d") and name[1:2].isdigit():
+        return decode_view(make_config("c" + name[1:], seed))
     small = {
         "c1_cached": lambda s: _c1(s or 1, cached_spans=True),
         # reduced copies of the big layouts: same structure, oracle-friendly size
