@@ -58,6 +58,7 @@ constexpr int kItemThreads = 1024;// plan_items work-group size
 // the work-groups reading them share one L2. An empty queue is left for the
 // next one (work stealing).
 constexpr int kQueues = 8;
+constexpr int kDecodeMaxSplits = 4096;   // key splits per (request, KV head) in decode at most
 
 // Header of the workspace (first 256 bytes).
 struct WsHeader {

@@ -36,10 +36,15 @@ __global__ void __launch_bounds__(64) decode_bf16_kernel(DecodeParams P) {
   const int l = threadIdx.x;
   const int n = l & 15;          // MFMA column: query head n of this KV head / key row of K
   const int j = l >> 4;          // lane group: d slice 8j..8j+7 of a chunk (QK), keys 4j..4j+3 (S, PV)
+  // Wave u runs on XCD u mod 8. The KV heads of one (request, split) are
+  // numbered so that they run on one XCD at about the same time and share
+  // the cos/sin rows of their keys in its L2: u = ((rs / 8) Hkv + g) 8 + rs mod 8.
   const int u = blockIdx.x;
-  const int s = u % P.nsplit;
-  const int g = (u / P.nsplit) % P.hkv;
-  const int r = u / (P.nsplit * P.hkv);
+  const int rs = (u / (kQueues * P.hkv)) * kQueues + u % kQueues;
+  if (rs >= P.num_reqs * P.nsplit) return;   // padding of the last group of 8
+  const int g = (u / kQueues) % P.hkv;
+  const int s = rs % P.nsplit;
+  const int r = rs / P.nsplit;
   const int64_t pslot = ((int64_t)(r * P.hkv + g) * P.nsplit + s) * G;
 
   // ---- the query's context index, block and descriptors (wave-uniform)
@@ -82,50 +87,94 @@ __global__ void __launch_bounds__(64) decode_bf16_kernel(DecodeParams P) {
     const __bf16* kc = (const __bf16*)P.k_cache + (int64_t)g * kBlock * D;
     const __bf16* vc = (const __bf16*)P.v_cache + (int64_t)g * kBlock * D;
     const float sl2 = P.scale_log2;
-    for (int b = b0; b < b1; ++b) {
-      const int sb = span[b];
-      const int fb = flg[b];
-      if (!(pdep_q || (fb & MINIPIC_BLK_GLOBAL) || sb == span_q)) continue;   // block invisible to the query
+    // rotation by this lane's key offset n within a block: cos(n theta_i),
+    // sin(n theta_i) for the lane's first-half elements i (rows n of the table)
+    float cd[ROPE ? NH * 8 : 1], sd[ROPE ? NH * 8 : 1];
+    const bool delta_ok = ROPE && P.max_pos >= kBlock;
+    if (delta_ok) {
+      const float* cs = P.cos_sin + (int64_t)n * D + 8 * j;
+#pragma unroll
+      for (int t = 0; t < NH; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          cd[8 * t + e] = cs[32 * t + e];
+          sd[8 * t + e] = cs[D / 2 + 32 * t + e];
+        }
+    }
+    // the next block of the split the query sees, or b1
+    auto next_visible = [&](int b) {
+      for (; b < b1; ++b)
+        if (pdep_q || (flg[b] & MINIPIC_BLK_GLOBAL) || span[b] == span_q) break;
+      return b;
+    };
+    // K rows: lane (n, j) = key n of the block, d slices 8 j of every chunk;
+    // V^T operand: lane (n, j) = d row 16 mt + n, keys 4 j .. 4 j + 3; the
+    // key's logical position. An invalid block reads as zeros.
+    auto load_block = [&](int b, bf16x8 (&ka)[NC], s16x4 (&va)[NM], int& pos) {
       int ph = btab[b];
       if (ph < 0 || (int64_t)ph >= P.num_blocks) {
         if (l == 0) atomicOr(P.err, (uint32_t)MINIPIC_EW_BLOCK);
         ph = -1;
       }
-      // ---- K rows: lane (n, j) = key n of the block, d slices 8 j of every chunk
-      bf16x8 ka[NC];
       if (ph >= 0) {
         const __bf16* kr = kc + ph * group + n * D + 8 * j;
 #pragma unroll
         for (int t = 0; t < NC; ++t) ka[t] = *(const bf16x8*)(kr + 32 * t);
-      } else {
-#pragma unroll
-        for (int t = 0; t < NC; ++t) ka[t] = bf16x8{};
-      }
-      // V^T operand: lane (n, j) = d row 16 mt + n, keys 4 j .. 4 j + 3
-      s16x4 va[NM];
-      if (ph >= 0) {
         const __bf16* vr = vc + ph * group + n * kBlock + 4 * j;
 #pragma unroll
         for (int mt = 0; mt < NM; ++mt) va[mt] = *(const s16x4*)(vr + 16 * mt * kBlock);
       } else {
 #pragma unroll
+        for (int t = 0; t < NC; ++t) ka[t] = bf16x8{};
+#pragma unroll
         for (int mt = 0; mt < NM; ++mt) va[mt] = s16x4{0, 0, 0, 0};
       }
+      pos = ROPE ? lpos[b * kBlock + n] : 0;
+    };
+    // one block in flight ahead of the one being computed
+    bf16x8 ka_n[NC];
+    s16x4 va_n[NM];
+    int pos_n = 0;
+    int b = next_visible(b0);
+    if (b < b1) load_block(b, ka_n, va_n, pos_n);
+    while (b < b1) {
+      bf16x8 ka[NC];
+      s16x4 va[NM];
+#pragma unroll
+      for (int t = 0; t < NC; ++t) ka[t] = ka_n[t];
+#pragma unroll
+      for (int mt = 0; mt < NM; ++mt) va[mt] = va_n[mt];
+      int pos = pos_n;
+      const int bc = b;
+      b = next_visible(b + 1);
+      if (b < b1) load_block(b, ka_n, va_n, pos_n);
       if (ROPE) {
         // rotate-half at the key's logical position: element i (first half)
         // with element i + D/2, in fp32, one rounding to bf16
-        int pos = lpos[b * kBlock + n];
         if (pos < 0 || pos >= P.max_pos) {
           atomicOr(P.err, (uint32_t)MINIPIC_EW_POS);
           pos = pos < 0 ? 0 : P.max_pos - 1;
         }
-        const float* cs = P.cos_sin + (int64_t)pos * D + 8 * j;
+        // consecutive positions p0 .. p0+15 (the usual case): read only row
+        // p0, shared by the block's 16 keys, and add the angle n theta_i;
+        // otherwise read each key's own row
+        const int p0 = __builtin_amdgcn_readfirstlane(pos);   // lane 0 holds key 0
+        const bool cons = delta_ok && __all(pos == p0 + n);
+        const float* cs = P.cos_sin + (int64_t)(cons ? p0 : pos) * D + 8 * j;
 #pragma unroll
         for (int t = 0; t < NH; ++t) {
           const f32x4 c0 = *(const f32x4*)(cs + 32 * t), c1 = *(const f32x4*)(cs + 32 * t + 4);
           const f32x4 s0 = *(const f32x4*)(cs + D / 2 + 32 * t), s1 = *(const f32x4*)(cs + D / 2 + 32 * t + 4);
-          const float cv[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
-          const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+          float cv[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+          float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+          if (cons) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float cb = cv[e], sb = sv[e];
+              cv[e] = cb * cd[8 * t + e] - sb * sd[8 * t + e];
+              sv[e] = sb * cd[8 * t + e] + cb * sd[8 * t + e];
+            }
+          }
           const u32x4 ua = __builtin_bit_cast(u32x4, ka[t]);
           const u32x4 ub = __builtin_bit_cast(u32x4, ka[t + NH]);
           u32x4 ra, rb;
@@ -145,7 +194,7 @@ __global__ void __launch_bounds__(64) decode_bf16_kernel(DecodeParams P) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int t = 0; t < NC; ++t) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[t], qf[t], acc, 0, 0, 0);
-      if (b == bq) {   // causal diagonal: keys after the query
+      if (bc == bq) {   // causal diagonal: keys after the query
         const int lim = c - bq * kBlock - 4 * j;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -189,42 +238,80 @@ __global__ void __launch_bounds__(64) decode_bf16_kernel(DecodeParams P) {
 }
 
 // Merge of the splits of one (request, query head): O = sum_s 2^(m_s - m*) O_s /
-// sum_s 2^(m_s - m*) l_s, m* = max_s m_s, summed in split order. One wave per
-// (request, query head); each lane owns D/64 consecutive elements.
+// sum_s 2^(m_s - m*) l_s, m* = max_s m_s. One 256-thread work-group per
+// (request, query head): the split weights are computed in parallel into LDS;
+// wave w sums splits w, w + 4, ... (several loads in flight), each lane D/64
+// consecutive elements; the four partial sums are added in wave order.
 template <int D>
-__global__ void __launch_bounds__(64) decode_merge_kernel(DecodeParams P, int G) {
+__global__ void __launch_bounds__(256) decode_merge_kernel(DecodeParams P, int G) {
   constexpr int E = D / 64;
-  const int l = threadIdx.x;
+  constexpr int UNR = 4;
+  __shared__ float w_s[kDecodeMaxSplits];
+  __shared__ float red[256 / 64][2];
+  __shared__ float part[256 / 64 - 1][D];
+  const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
   const int h = blockIdx.x % P.hq;
   const int r = blockIdx.x / P.hq;
   const int g = h / G, n = h % G;
-  const int64_t base = (int64_t)(r * P.hkv + g) * P.nsplit * G + n;   // split s at base + s G
-  float mstar = -INFINITY;
-  for (int s = l; s < P.nsplit; s += 64) mstar = fmaxf(mstar, P.part_ml[base + (int64_t)s * G].x);
+  const int ns = P.nsplit;
+  const int64_t base = (int64_t)(r * P.hkv + g) * ns * G + n;   // split s at base + s G
+  float mloc = -INFINITY;
+  for (int s = tid; s < ns; s += 256) mloc = fmaxf(mloc, P.part_ml[base + (int64_t)s * G].x);
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) mstar = fmaxf(mstar, __shfl_xor(mstar, o, 64));
+  for (int o = 32; o >= 1; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o, 64));
+  if (l == 0) red[w][0] = mloc;
+  __syncthreads();
+  const float mstar = fmaxf(fmaxf(red[0][0], red[1][0]), fmaxf(red[2][0], red[3][0]));
+  float dloc = 0.f;
+  for (int s = tid; s < ns; s += 256) {
+    const float2 ml = P.part_ml[base + (int64_t)s * G];
+    const float wt = ml.x == -INFINITY ? 0.f : exp2f(ml.x - mstar);
+    w_s[s] = wt;
+    dloc += wt * ml.y;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) dloc += __shfl_xor(dloc, o, 64);
+  if (l == 0) red[w][1] = dloc;
+  __syncthreads();
+  const float den = (red[0][1] + red[1][1]) + (red[2][1] + red[3][1]);
   float num[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) num[e] = 0.f;
-  float den = 0.f;
-  for (int s = 0; s < P.nsplit; ++s) {
-    const int64_t ps = base + (int64_t)s * G;
-    const float2 ml = P.part_ml[ps];
-    if (ml.x == -INFINITY) continue;   // split without visible keys
-    const float w = exp2f(ml.x - mstar);
-    den += w * ml.y;
+  const float* po = P.part_o + base * D + E * l;
+  for (int s0 = w; s0 < ns; s0 += 4 * UNR) {
+    float v[UNR][E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) num[e] += w * P.part_o[ps * D + E * l + e];
+    for (int k = 0; k < UNR; ++k) {
+      const int s = s0 + 4 * k;
+#pragma unroll
+      for (int e = 0; e < E; ++e) v[k][e] = s < ns ? po[(int64_t)s * G * D + e] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < UNR; ++k) {
+      const int s = s0 + 4 * k;
+      const float wt = s < ns ? w_s[s] : 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) num[e] += wt * v[k][e];
+    }
   }
-  const float inv = 1.f / den;
-  __bf16* op = (__bf16*)P.out + ((int64_t)r * P.hq + h) * D + E * l;
+  if (w > 0) {
 #pragma unroll
-  for (int e = 0; e < E; ++e) op[e] = (__bf16)(num[e] * inv);
+    for (int e = 0; e < E; ++e) part[w - 1][E * l + e] = num[e];
+  }
+  __syncthreads();
+  if (w == 0) {
+    const float inv = 1.f / den;
+    __bf16* op = (__bf16*)P.out + ((int64_t)r * P.hq + h) * D + E * l;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      op[e] = (__bf16)((((num[e] + part[0][E * l + e]) + part[1][E * l + e]) + part[2][E * l + e]) * inv);
+  }
 }
 
 template <int D, bool ROPE>
 static hipError_t launch_dec_g(const DecodeParams& p, int G, hipStream_t s) {
-  const dim3 grid((unsigned)((int64_t)p.num_reqs * p.hkv * p.nsplit));
+  const int64_t groups = ((int64_t)p.num_reqs * p.nsplit + kQueues - 1) / kQueues;
+  const dim3 grid((unsigned)(groups * kQueues * p.hkv));
   switch (G) {
     case 1: hipLaunchKernelGGL((decode_bf16_kernel<D, 1, ROPE>), grid, dim3(64), 0, s, p); break;
     case 2: hipLaunchKernelGGL((decode_bf16_kernel<D, 2, ROPE>), grid, dim3(64), 0, s, p); break;
@@ -243,8 +330,8 @@ hipError_t launch_decode_bf16(const DecodeParams& p, int D, int G, bool rope, hi
 
 hipError_t launch_decode_merge(const DecodeParams& p, int D, int G, hipStream_t s) {
   const dim3 grid((unsigned)((int64_t)p.num_reqs * p.hq));
-  if (D == 128) hipLaunchKernelGGL((decode_merge_kernel<128>), grid, dim3(64), 0, s, p, G);
-  else if (D == 64) hipLaunchKernelGGL((decode_merge_kernel<64>), grid, dim3(64), 0, s, p, G);
+  if (D == 128) hipLaunchKernelGGL((decode_merge_kernel<128>), grid, dim3(256), 0, s, p, G);
+  else if (D == 64) hipLaunchKernelGGL((decode_merge_kernel<64>), grid, dim3(256), 0, s, p, G);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -111,8 +111,9 @@ hipError_t timer_mark(int i, hipStream_t s) {
 }
 
 // Decode plan (host scalars only): key splits per (request, KV head) so that
-// about kDecodeWaves waves cover the batch, every split at least two blocks.
-constexpr int64_t kDecodeWaves = 4096;
+// about kDecodeWaves waves (one round at two waves per SIMD on 256 CUs) cover
+// the batch, every split at least two blocks, at most kDecodeMaxSplits splits.
+constexpr int64_t kDecodeWaves = 2048;
 struct DecodePlan {
   int split_blocks, nsplit;
   size_t off_ml, off_o, bytes;
@@ -123,6 +124,7 @@ void make_decode_plan(const minipic_batch* b, DecodePlan* p) {
   const int64_t per = (int64_t)b->num_reqs * b->num_kv_heads * MB;
   int64_t sb = (per + kDecodeWaves - 1) / kDecodeWaves;
   if (sb < 2) sb = 2;
+  if ((MB + sb - 1) / sb > kDecodeMaxSplits) sb = (MB + kDecodeMaxSplits - 1) / kDecodeMaxSplits;
   p->split_blocks = (int)sb;
   p->nsplit = (int)((MB + sb - 1) / sb);
   const int64_t parts = (int64_t)b->num_reqs * b->num_q_heads * p->nsplit;   // (request, KV head, split, head in group)
