@@ -61,6 +61,10 @@ WORKLOADS = {
           "Hq 32, Hkv 8, d 128, bf16, RoPE base 5e5",
     "c5": "70B shape: 8 requests, shared cached 256-token GLOBAL prefix + 20 fresh SSep spans of U{128..512} "
           "padded to 16 + 128-token PDep question; Hq 64, Hkv 8, d 128, bf16, RoPE base 5e5",
+    "e2": "C2 with each span's first block recomputed against all earlier context (EPIC / LegoLink) and the "
+          "rest of the span an SSep span that sees it",
+    "e4": "C4's context, every span cached except its first block, recomputed against all earlier context "
+          "(EPIC / LegoLink), + the 512-token PDep suffix",
 }
 
 
@@ -72,8 +76,11 @@ def parse():
     ap.add_argument("--config", default="c4", choices=sorted(k for k in WORKLOADS if k.startswith("c")))
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample (0 disables the cpu_baseline leg)")
-    ap.add_argument("--suite", default="c2,c3,c5,d2,d3,d4,d5",
+    ap.add_argument("--suite", default="c2,c3,c5,e2,e4,d2,d3,d4,d5",
                     help="other workloads whose attention is timed beside the main one (empty: none)")
+    ap.add_argument("--sweeps", action="store_true",
+                    help="only run the kernel sweeps that mirror the pages' preload / TTFT figure and print "
+                         "one JSON line per point")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
@@ -328,6 +335,49 @@ def suite_entry(name, reps):
     return e
 
 
+def sweeps(reps=10):
+    """Kernel-level mirror of the pages' preload / time-to-first-token figure (one
+    attention layer, 8B shape): (a) one causal prompt of N tokens, no spans;
+    (b) n documents of 1000 tokens (padded to 1008) prefilled together as SSep
+    spans of one request; (c) n such documents cached and a 64-token PDep
+    question computed, against the same with every document fresh."""
+    import torch
+    import workload
+    from workload import Segment
+    from position_independent_paged_amd import metrics
+    from position_independent_paged_amd.staging import DeviceWorkload
+    shape = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16", rope_theta=5e5)
+
+    def point(sweep, x, segs, **extra):
+        L = sum(sg.length for sg in segs)
+        w = workload.custom(f"{sweep}{x}", [segs], max_pos=max(32768, L), seed=x, **shape)
+        dw = DeviceWorkload(w, device="cuda:0")
+        dw.write_new()
+        for _ in range(2):
+            dw.attend()
+            dw.attend_prerotated()
+        torch.cuda.synchronize()
+        plan, attn, merge = kernel_ms(dw.attend, reps)
+        prerot = kernel_ms(dw.attend_prerotated, reps)[1]
+        flops = metrics.attention_flops(metrics.workload_pairs(w), w.num_q_heads, w.head_dim)
+        rec = {"sweep": sweep, "x": x, "context_tokens": int(L), "query_tokens": int(w.total_q),
+               "call_ms": round(plan + attn + merge, 5), "attention_kernel_ms": round(attn, 5),
+               "prerotated_kernel_ms": round(prerot, 5), "rope_overhead_pct": round(100 * (attn / prerot - 1), 2),
+               "tflops_kernel": round(flops / (attn * 1e-3) / 1e12, 1), **extra}
+        print(json.dumps(rec), flush=True)
+        del dw
+        torch.cuda.empty_cache()
+
+    for n in [1024, 2048, 4096, 8192, 16384, 32768]:
+        point("prompt_length", n, [Segment("pdep", n)])
+    for n in [1, 2, 4, 8, 16, 32]:
+        point("doc_count_preload", n, [Segment("span", 1008) for _ in range(n)])
+    for n in [1, 2, 4, 8, 16, 32]:
+        point("doc_count_question_cached", n, [Segment("span", 1008, fresh=False) for _ in range(n)] +
+              [Segment("pdep", 64)])
+        point("doc_count_question_fresh", n, [Segment("span", 1008) for _ in range(n)] + [Segment("pdep", 64)])
+
+
 def main():
     a = parse()
     if a.summarize_counters:
@@ -352,6 +402,9 @@ def main():
     torch.cuda.set_device(0)
     if a.calibrate_copy:
         calibrate_copy()
+        return
+    if a.sweeps:
+        sweeps()
         return
     log(f"[bench] generating {a.config}")
     w = workload.make_config(a.config)

@@ -139,7 +139,8 @@ def test_write_kv_scattered_and_skipped_slots():
 # attention parity
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["c1", "c1_cached", "c3_small", "c4_small", "c5_small", "c2", "c3"])
+@pytest.mark.parametrize("name", ["c1", "c1_cached", "c3_small", "c4_small", "c5_small", "c2", "c3", "e2",
+                                  "e4_small"])
 def test_parity_all_rows(name):
     w = workload.make_config(name)
     say(f"parity {name}: dtype={w.dtype} R={w.num_reqs} total_q={w.total_q} max_ctx={w.max_ctx_len}")
@@ -152,7 +153,7 @@ def test_parity_all_rows(name):
     check(name, got, want, w.dtype)
 
 
-@pytest.mark.parametrize("name,rows", [("c4", 384), ("c5", 96)])
+@pytest.mark.parametrize("name,rows", [("c4", 384), ("c5", 96), ("e4", 384)])
 def test_parity_sampled_full_size(name, rows):
     w = workload.make_config(name)
     say(f"parity(sampled) {name}: total_q={w.total_q} max_ctx={w.max_ctx_len}")

@@ -362,7 +362,43 @@ def _c5(seed=5, num_reqs=8, n_spans=20, lo=128, hi=512, prefix=256, q_len=128, n
                  head_dim=128, dtype="bf16", rope_theta=5e5, max_pos=32768, seed=seed, rng=rng)
 
 
+def _epic(name, seed, spans, recompute, head, tail, fresh_rest, **shape):
+    """Spans whose first `recompute` tokens (block-rounded) are recomputed against
+    all preceding context (a PDep segment) while the rest of the span keeps its
+    span id, so the span's later queries still see its recomputed start."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    segs, ids = [], []
+    if head:
+        segs.append(Segment("span", head))
+        ids.append(0)
+    for i, n in enumerate(spans):
+        sid = len(ids)
+        segs += [Segment("pdep", recompute), Segment("span", n - recompute, fresh=fresh_rest)]
+        ids += [sid, sid]
+    segs.append(Segment("pdep", tail))
+    ids.append(len(ids))
+    return build(name, [segs], seed=seed, rng=rng, span_ids=[np.array(ids)], **shape)
+
+
+_SHAPE_8B = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16", rope_theta=5e5, max_pos=32768)
+
+
+def _e2(seed=2, name="e2"):
+    """C2's layout with the first block of each span recomputed against the
+    system prompt and earlier spans (EPIC / LegoLink); the rest of each span is
+    computed as an SSep span that sees its recomputed start."""
+    return _epic(name, seed, [192] * 10, 16, 512, 64, True, **_SHAPE_8B)
+
+
+def _e4(seed=4, name="e4", n_spans=120):
+    """C4's context with every span cached except its first block, which is
+    recomputed against all preceding context; then the 512-token PDep suffix."""
+    return _epic(name, seed, [256] * n_spans, 16, 0, 512, False, **_SHAPE_8B)
+
+
 CONFIGS = {
+    "e2": _e2,
+    "e4": _e4,
     "c1": _c1,
     "c2": _c2,
     "c3": _c3,
@@ -413,6 +449,7 @@ def make_config(name: str, seed: Optional[int] = None) -> Workload:
         "c3_small": lambda s: _c3(s or 3, num_reqs=4, pool=8, per_req=4, q_len=48, name="c3_small"),
         "c4_small": lambda s: _c4(s or 4, n_spans=12, span_len=256, suffix=200, name="c4_small"),
         "c5_small": lambda s: _c5(s or 5, num_reqs=2, n_spans=4, prefix=64, q_len=40, name="c5_small"),
+        "e4_small": lambda s: _e4(s or 4, name="e4_small", n_spans=12),
     }
     if name in small:
         return small[name](seed)
