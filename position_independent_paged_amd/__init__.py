@@ -5,7 +5,8 @@ package is its thin Python binding plus device staging helpers. The library
 is loaded on the first call into it (or by ``load_library()``), which raises
 ImportError if it has not been built: there is no fallback path.
 """
-from ._binding import (EXPORTS, MINIPIC_BF16, MINIPIC_BLK_GLOBAL, MINIPIC_BLK_PDEP, MINIPIC_EW_BLOCK,
+from ._binding import (BlockCache, MINIPIC_ERR_CACHE_FULL, MINIPIC_ERR_CONTRACT, minipic_describe_blocks,
+                       minipic_slot_mapping, EXPORTS, MINIPIC_BF16, MINIPIC_BLK_GLOBAL, MINIPIC_BLK_PDEP, MINIPIC_EW_BLOCK,
                        MINIPIC_EW_CTX, MINIPIC_EW_POS, MINIPIC_EW_QCTX, MINIPIC_F32, MINIPIC_FLAG_ROTATE_Q,
                        LIB_PATH, MinipicError, load_library, minipic_batch, minipic_get_launch_info,
                        minipic_decode_attn, minipic_decode_prerotated, minipic_decode_workspace_size,
@@ -15,6 +16,7 @@ from ._binding import (EXPORTS, MINIPIC_BF16, MINIPIC_BLK_GLOBAL, MINIPIC_BLK_PD
 
 
 __all__ = [
+    "BlockCache", "MINIPIC_ERR_CACHE_FULL", "MINIPIC_ERR_CONTRACT", "minipic_describe_blocks", "minipic_slot_mapping",
     "EXPORTS", "LIB_PATH", "MinipicError", "load_library", "minipic_batch", "minipic_get_launch_info",
     "minipic_prefill_attn", "minipic_reference_prerotated", "minipic_rope_table", "minipic_version",
     "minipic_set_kernel_timing", "minipic_kernel_times", "minipic_decode_workspace_size",

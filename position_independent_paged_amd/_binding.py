@@ -30,7 +30,19 @@ EXPORTS = [
     "minipic_write_kv", "minipic_workspace_size", "minipic_get_launch_info", "minipic_prefill_attn",
     "minipic_reference_prerotated", "minipic_set_kernel_timing", "minipic_kernel_times",
     "minipic_decode_workspace_size", "minipic_decode_attn", "minipic_decode_prerotated",
+    "minipic_describe_blocks", "minipic_block_cache_create", "minipic_block_cache_destroy",
+    "minipic_block_cache_assign", "minipic_slot_mapping",
 ]
+
+
+MINIPIC_ERR_CONTRACT = -5
+MINIPIC_ERR_CACHE_FULL = -6
+
+
+class minipic_markers(ctypes.Structure):
+    """Marker token ids (-1 disables one) and the hash seed h_0."""
+    _fields_ = [("ssep", ctypes.c_int32), ("pdep", ctypes.c_int32), ("global_", ctypes.c_int32),
+                ("seed", ctypes.c_uint64)]
 
 
 class MinipicError(RuntimeError):
@@ -87,10 +99,19 @@ def load_library(path: str = LIB_PATH):
     lib.minipic_decode_attn.argtypes = attn
     lib.minipic_decode_prerotated.argtypes = [vp, vp, vp, i64, ctypes.POINTER(minipic_batch), ctypes.c_float, vp,
                                               vp, sz, ctypes.c_uint32, i32, vp]
+    lib.minipic_describe_blocks.argtypes = [vp, i64, ctypes.POINTER(minipic_markers), i32, vp, vp, vp, i64,
+                                            ctypes.POINTER(i64)]
+    lib.minipic_block_cache_create.argtypes = [i64]
+    lib.minipic_block_cache_create.restype = ctypes.c_void_p
+    lib.minipic_block_cache_destroy.argtypes = [ctypes.c_void_p]
+    lib.minipic_block_cache_destroy.restype = None
+    lib.minipic_block_cache_assign.argtypes = [ctypes.c_void_p, vp, i64, vp, vp, ctypes.POINTER(i64)]
+    lib.minipic_slot_mapping.argtypes = [vp, vp, i64, i32, vp, vp, ctypes.POINTER(i64)]
     lib.minipic_set_kernel_timing.argtypes = [ctypes.c_int]
     lib.minipic_kernel_times.argtypes = [ctypes.POINTER(ctypes.c_float)]
     for name in EXPORTS[3:]:
-        getattr(lib, name).restype = ctypes.c_int
+        if name not in ("minipic_block_cache_create", "minipic_block_cache_destroy"):
+            getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -197,3 +218,64 @@ def minipic_decode_prerotated(q, k_cache, v_cache, num_blocks, batch, out, works
         _ptr(q), _ptr(k_cache), _ptr(v_cache), int(num_blocks), ctypes.byref(batch), float(softmax_scale),
         _ptr(out), _ptr(workspace), int(workspace.numel() * workspace.element_size()), int(flags),
         _dtype_code(q), _stream(stream)))
+
+
+def _np_ptr(a):
+    return ctypes.c_void_p(a.ctypes.data) if a is not None and a.size else None
+
+
+def minipic_describe_blocks(tokens, *, ssep=-1, pdep=-1, global_=-1, seed=0):
+    """(hashes uint64, span_id int32, flags uint8) of one request's blocks."""
+    import numpy as np
+    tok = np.ascontiguousarray(tokens, dtype=np.int32)
+    nb = (len(tok) + 15) // 16
+    hashes = np.zeros(max(nb, 1), np.uint64)
+    span = np.zeros(max(nb, 1), np.int32)
+    flags = np.zeros(max(nb, 1), np.uint8)
+    m = minipic_markers(ssep, pdep, global_, seed)
+    out = ctypes.c_int64(0)
+    _check(load_library().minipic_describe_blocks(_np_ptr(tok), len(tok), ctypes.byref(m), 16, _np_ptr(hashes),
+                                                  _np_ptr(span), _np_ptr(flags), nb, ctypes.byref(out)))
+    return hashes[:nb], span[:nb], flags[:nb]
+
+
+class BlockCache:
+    """Hash -> physical block map of the library (host memory)."""
+
+    def __init__(self, num_blocks: int):
+        self._lib = load_library()
+        self._h = self._lib.minipic_block_cache_create(int(num_blocks))
+        if not self._h:
+            raise MinipicError(MINIPIC_ERR_INVALID_ARG, "minipic_block_cache_create failed")
+
+    def assign(self, hashes):
+        """(block_table int32, hit uint8, num_hits) for one request's block hashes."""
+        import numpy as np
+        h = np.ascontiguousarray(hashes, dtype=np.uint64)
+        bt = np.zeros(max(len(h), 1), np.int32)
+        hit = np.zeros(max(len(h), 1), np.uint8)
+        n = ctypes.c_int64(0)
+        _check(self._lib.minipic_block_cache_assign(ctypes.c_void_p(self._h), _np_ptr(h), len(h), _np_ptr(bt),
+                                                    _np_ptr(hit), ctypes.byref(n)))
+        return bt[:len(h)], hit[:len(h)], int(n.value)
+
+    def close(self):
+        if self._h:
+            self._lib.minipic_block_cache_destroy(ctypes.c_void_p(self._h))
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+
+def minipic_slot_mapping(block_table, hit, n: int):
+    """(slots int64, ctx_index int32) of the tokens whose blocks missed."""
+    import numpy as np
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    hi = np.ascontiguousarray(hit, dtype=np.uint8)
+    slots = np.zeros(max(n, 1), np.int64)
+    idx = np.zeros(max(n, 1), np.int32)
+    k = ctypes.c_int64(0)
+    _check(load_library().minipic_slot_mapping(_np_ptr(bt), _np_ptr(hi), int(n), 16, _np_ptr(slots), _np_ptr(idx),
+                                               ctypes.byref(k)))
+    return slots[:k.value], idx[:k.value]

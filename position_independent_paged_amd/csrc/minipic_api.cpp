@@ -10,6 +10,7 @@
 #include <string>
 
 #include "../../include/minipic.h"
+#include "../../include/minipic_desc.h"
 #include "common.h"
 
 namespace minipic {
@@ -384,6 +385,10 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, int64
 
 }  // namespace
 
+namespace minipic_host {
+int set_error(int code, const std::string& msg) { return fail(code, "%s", msg.c_str()); }
+}  // namespace minipic_host
+
 extern "C" {
 
 const char* minipic_version(void) { return "minipic-mi355x 0.1.0 (gfx950)"; }
@@ -395,6 +400,8 @@ const char* minipic_status_string(int status) {
     case MINIPIC_ERR_UNSUPPORTED: return "unsupported configuration";
     case MINIPIC_ERR_WORKSPACE: return "workspace too small";
     case MINIPIC_ERR_HIP: return "HIP error";
+    case MINIPIC_ERR_CONTRACT: return "marker contract violated";
+    case MINIPIC_ERR_CACHE_FULL: return "block cache full";
   }
   return "unknown status";
 }

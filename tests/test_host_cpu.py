@@ -1,9 +1,10 @@
 """CPU-only checks of the library boundary and host logic (no GPU needed).
 
 The library must load and export every entry point declared in
-include/minipic.h; every invalid call must be rejected by host-side checks
-before any HIP call is made.
+include/*.h; every invalid call must be rejected by host-side checks before
+any HIP call is made.
 """
+import glob
 import ctypes
 import os
 import re
@@ -21,9 +22,12 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def header_functions():
-    with open(os.path.join(ROOT, "include", "minipic.h")) as f:
-        text = f.read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(minipic_\w+)\s*\(", text, re.M)))
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        with open(h) as f:
+            text = f.read()
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(minipic_\w+)\s*\(", text, re.M))
+    return sorted(names)
 
 
 def test_library_exports_every_header_symbol():
