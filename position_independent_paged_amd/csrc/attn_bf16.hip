@@ -50,8 +50,11 @@ constexpr int kKT = 32;           // keys per pipeline step
 constexpr int kListMax = 256;     // list entries staged in LDS per pass
 // Sentinel entries after the last one of a pass (no block: loads return
 // zeros, never visible, never full), so the look-ups of the steps past the
-// end need no bounds test and the step body stays free of branches.
-constexpr int kListPad = 8;
+// end need no bounds test and the step body stays free of branches. Step s
+// issues the K loads of step s + 4 (entries 2s + 8, 2s + 9); with nsteps =
+// ceil(n / 2) the last index reached is n + 8.
+constexpr int kLoadAhead = 4;
+constexpr int kListPad = 2 * kLoadAhead + 2;
 constexpr int kRsrcWord3 = 0x00020000;  // buffer descriptor word 3 (gfx9, raw dword access)
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -247,14 +250,17 @@ __device__ __forceinline__ void store_v(const StepCtx<D, RB>& cx, int buf, const
   }
 }
 
-// S^T for the 32 keys in K buffer `buf`, all row blocks of the wave.
+// S^T - m for the 32 keys in K buffer `buf`, all row blocks of the wave: the
+// MFMA chain starts from `bias` (every element of a lane is minus the running
+// max of the lane's query row), so the scores leave the MFMA already shifted.
 template <int D, int RB>
-__device__ __forceinline__ void qk(const StepCtx<D, RB>& cx, int buf, const bf16x8 (&qf)[RB][D / 16], f32x16 (&s)[RB]) {
+__device__ __forceinline__ void qk(const StepCtx<D, RB>& cx, int buf, const bf16x8 (&qf)[RB][D / 16],
+                                   const f32x16 (&bias)[RB], f32x16 (&s)[RB]) {
   using C = Cfg<D, RB>;
   const int lane = threadIdx.x & 63;
   const __bf16* kb_ = cx.kl + buf * C::KSZ + (lane & 31) * C::KSTR + 8 * (lane >> 5);
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) s[rb] = f32x16{};
+  for (int rb = 0; rb < RB; ++rb) s[rb] = bias[rb];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
     const bf16x8 a = *(const bf16x8*)(kb_ + 16 * ks);
@@ -263,13 +269,10 @@ __device__ __forceinline__ void qk(const StepCtx<D, RB>& cx, int buf, const bf16
   }
 }
 
-// O^T += V^T P^T for the 32 keys in V buffer `buf`, all row blocks of the
-// wave. The row sums of P come from the same MFMA with a constant A operand
-// whose first row is all ones: lsum[rb] element 0 of lane l (l < 32) is the
-// running sum of row l, summed from the bf16 P the numerator uses.
+// O^T += V^T P^T for the 32 keys in V buffer `buf`, all row blocks of the wave.
 template <int D, int RB>
 __device__ __forceinline__ void pv(const StepCtx<D, RB>& cx, int buf, const bf16x8 (&pk)[RB][2],
-                                   f32x16 (&o)[RB][D / 32], f32x16 (&lsum)[RB], const bf16x8& ones) {
+                                   f32x16 (&o)[RB][D / 32]) {
   using C = Cfg<D, RB>;
   const int lane = threadIdx.x & 63;
   const __bf16* vb_ = cx.vl + buf * C::VSZ + (lane & 31) * C::VSTR + 8 * (lane >> 5);
@@ -281,10 +284,6 @@ __device__ __forceinline__ void pv(const StepCtx<D, RB>& cx, int buf, const bf16
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) o[rb][dg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[rb][sh], o[rb][dg], 0, 0, 0);
     }
-#pragma unroll
-  for (int sh = 0; sh < 2; ++sh)
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) lsum[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pk[rb][sh], lsum[rb], 0, 0, 0);
 }
 
 // true when every row of the tile sees every key of step j (uniform)
@@ -313,73 +312,76 @@ __device__ __forceinline__ void apply_mask(const StepCtx<D, RB>& cx, int j, cons
   }
 }
 
-// P = exp2(S * scale_log2 - m) rounded to bf16 in the B-operand layout of the
-// PV MFMA; the row sums accumulate in fp32.
+// P = exp2(S - m) rounded to bf16 in the B-operand layout of the PV MFMA
+// (the scores are already in log2 units and shifted by the running max). The
+// lane's share of the row sum adds the same bf16 values the numerator uses,
+// two per v_dot2_f32_bf16 against (1, 1). (The packed word goes to the dot
+// product before it is inserted into the vector: taking it back out of the
+// vector made hipcc read the first word of the quad four times.)
 template <int RB>
-__device__ __forceinline__ void softmax_p(const f32x16 (&s)[RB], float sl2, const float (&m_run)[RB],
-                                          bf16x8 (&pk)[RB][2]) {
+__device__ __forceinline__ void softmax_p(const f32x16 (&s)[RB], bf16x8 (&pk)[RB][2], float (&lsum)[RB]) {
+  const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const float m_use = (m_run[rb] == -INFINITY) ? 0.f : m_run[rb];
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int sh = 0; sh < 2; ++sh) {
       u32x4 u;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[rb][8 * sh + 2 * j], sl2, -m_use));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[rb][8 * sh + 2 * j + 1], sl2, -m_use));
-        u[j] = pack_bf16x2(p0, p1);
+        const uint32_t w = pack_bf16x2(__builtin_amdgcn_exp2f(s[rb][8 * sh + 2 * j]), __builtin_amdgcn_exp2f(s[rb][8 * sh + 2 * j + 1]));
+        lsum[rb] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one2, lsum[rb], false);
+        u[j] = w;
       }
       pk[rb][sh] = __builtin_bit_cast(bf16x8, u);
     }
-  }
 }
 
-// row max of S (scaled to log2 units), both halves of the lane pair
+// max of the lane's 16 shifted scores (one half of its query row)
+__device__ __forceinline__ float lane_max(const f32x16& s) {
+  float m = fmaxf(fmaxf(s[0], s[1]), s[2]);
+#pragma unroll
+  for (int i = 3; i + 1 < 16; i += 2) m = fmaxf(fmaxf(m, s[i]), s[i + 1]);
+  return fmaxf(m, s[15]);
+}
+
+// Running-max state of the lane's query rows. The max is raised lazily: only
+// when a shifted score exceeds `thr` (2^8 while the row has a max; -inf
+// before its first visible key, when the shift is 0).
 template <int RB>
-__device__ __forceinline__ void row_max(const f32x16 (&s)[RB], float sl2, float (&ms)[RB]) {
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    float mx = s[rb][0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[rb][i]);
-    ms[rb] = xor32_max(mx) * sl2;
-  }
-}
+struct MaxState {
+  float m[RB];        // running max in log2 units (-inf: no visible key yet)
+  float thr[RB];
+  f32x16 bias[RB];    // -m, or 0 while m is -inf (the QK MFMA's C operand)
+};
 
-// Raise the running max where the scores of the coming step need it
-// (lazily: only when a row max grows by more than 2^8).
+// Shift the rows whose scores crossed the threshold to their new max: the
+// scores of this step, the bias of the next ones, O and the row sums.
 template <int D, int RB>
-__device__ __forceinline__ void raise_max(const float (&ms)[RB], float (&m_run)[RB], f32x16 (&lsum)[RB],
-                                          f32x16 (&o)[RB][D / 32]) {
+__device__ __forceinline__ void raise_max(const float (&mx)[RB], MaxState<RB>& ms, f32x16 (&sc)[RB],
+                                          float (&lsum)[RB], f32x16 (&o)[RB][D / 32]) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
-    if (__any(ms[rb] > m_run[rb] + 8.0f)) {
-      const float m_new = fmaxf(m_run[rb], ms[rb]);
-      const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run[rb] - m_new);
+    const float rm = xor32_max(mx[rb]);           // shifted row max
+    const bool up = rm > ms.thr[rb];
+    const float delta = up ? rm : 0.f;
+    const float m_old = ms.m[rb];
+    const float m_new = (m_old == -INFINITY ? 0.f : m_old) + delta;
+    const float alpha = up ? exp2f(m_old - m_new) : 1.f;   // 0 for a first max (O, l are zero)
 #pragma unroll
-      for (int dg = 0; dg < D / 32; ++dg)
+    for (int dg = 0; dg < D / 32; ++dg)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[rb][dg][i] *= alpha;
+      for (int i = 0; i < 16; ++i) o[rb][dg][i] *= alpha;
+    lsum[rb] *= alpha;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) lsum[rb][i] *= alpha;
-      m_run[rb] = m_new;
+    for (int i = 0; i < 16; ++i) {
+      sc[rb][i] -= delta;
+      ms.bias[rb][i] -= delta;
+    }
+    if (up) {
+      ms.m[rb] = m_new;
+      ms.thr[rb] = 8.0f;
     }
   }
-}
-
-// Instruction-scheduling hint for the MFMA part of a step (masks of
-// __builtin_amdgcn_sched_group_barrier: 0x008 MFMA, 0x100 LDS read): the
-// operand reads from LDS run two reads ahead of the MFMAs that use them.
-template <int NRD, int RB>
-__device__ __forceinline__ void sched_mfma() {
-  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-  for (int i = 0; i < NRD; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);
-    if (i + 2 < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, 2 * RB, 0);
 }
 
 template <int D, int G, bool ROPE, int RB>
@@ -450,7 +452,17 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
       const __bf16* qp = (const __bf16*)P.q + qoff[rb];
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) qf[rb][ks] = valid ? *(const bf16x8*)(qp + 16 * ks + 8 * h) : bf16x8{};
-      if ((P.flags & MINIPIC_FLAG_ROTATE_Q) && valid) {
+      // q is scaled by scale * log2(e) here, so that the MFMA gives the scores in
+      // log2 units (rounded to bf16 once with the rotation below)
+      if (!(P.flags & MINIPIC_FLAG_ROTATE_Q)) {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          u32x4 u = __builtin_bit_cast(u32x4, qf[rb][ks]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) u[j] = pack_bf16x2(bf16_lo(u[j]) * sl2, bf16_hi(u[j]) * sl2);
+          qf[rb][ks] = __builtin_bit_cast(bf16x8, u);
+        }
+      } else if (valid) {
         int pos = lpos[tk.c];
         if (pos < 0 || pos >= P.max_pos) {
           atomicOr(&P.hdr->err, (uint32_t)MINIPIC_EW_POS);
@@ -465,8 +477,8 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const int i0 = 16 * ks + 8 * h + 2 * j;
-            const float c_0 = cs[i0], c_1 = cs[i0 + 1];
-            const float s_0 = cs[D / 2 + i0], s_1 = cs[D / 2 + i0 + 1];
+            const float c_0 = cs[i0] * sl2, c_1 = cs[i0 + 1] * sl2;
+            const float s_0 = cs[D / 2 + i0] * sl2, s_1 = cs[D / 2 + i0 + 1] * sl2;
             const float a0 = bf16_lo(a[j]), a1 = bf16_hi(a[j]);
             const float b0 = bf16_lo(b[j]), b1 = bf16_hi(b[j]);
             ra[j] = pack_bf16x2(a0 * c_0 - b0 * s_0, a1 * c_1 - b1 * s_1);
@@ -483,17 +495,15 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
       for (int i = 0; i < NDG; ++i) o[rb][i] = f32x16{};
-    float m_run[RB];       // running max of scaled scores (log2 units)
-    f32x16 lsum[RB];       // running row sums (element 0 of lanes 0..31)
+    MaxState<RB> mst;
+    float lsum[RB];        // the lane's share of the running row sums (lanes l, l ^ 32 add up to row l % 32)
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      m_run[rb] = -INFINITY;
-      lsum[rb] = f32x16{};
+      mst.m[rb] = -INFINITY;
+      mst.thr[rb] = -INFINITY;
+      mst.bias[rb] = f32x16{};
+      lsum[rb] = 0.f;
     }
-    // A operand of the row-sum MFMA: row 0 all ones, other rows zero
-    bf16x8 ones;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ones[i] = (__bf16)(l32 == 0 ? 1.0f : 0.0f);
 
     for (int c0 = item.p0; c0 < item.p1; c0 += kListMax) {
       const int n_l = min(kListMax, item.p1 - c0);
@@ -543,47 +553,52 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
       cx.vl = vl;
 
       // ---- prologue: K(0), V(0), K(1) in LDS; S(0) (and for the leading
-      // waves P(0)); loads of K(2), V(1) in flight
-      St st, st1;
-      load_k<D, RB, ROPE>(cx, 0, st);
-      load_v<D, RB>(cx, 0, st);
-      load_k<D, RB, ROPE>(cx, 1, st1);
-      store_k<D, RB, ROPE>(cx, 0, st);
-      store_v<D, RB>(cx, 0, st);
-      load_k<D, RB, ROPE>(cx, 2, st);
-      load_v<D, RB>(cx, 1, st);
-      store_k<D, RB, ROPE>(cx, 1, st1);
+      // waves P(0)); loads of K(2), V(1) (stage sa) and K(3), V(2) (stage sb)
+      // in flight. Step s stores the stage it loaded two steps before, so each
+      // load has two steps to arrive.
+      St sa, sb;
+      load_k<D, RB, ROPE>(cx, 0, sa);
+      load_v<D, RB>(cx, 0, sa);
+      load_k<D, RB, ROPE>(cx, 1, sb);
+      store_k<D, RB, ROPE>(cx, 0, sa);
+      store_v<D, RB>(cx, 0, sa);
+      load_k<D, RB, ROPE>(cx, 2, sa);
+      load_v<D, RB>(cx, 1, sa);
+      store_k<D, RB, ROPE>(cx, 1, sb);
+      load_k<D, RB, ROPE>(cx, 3, sb);
+      load_v<D, RB>(cx, 2, sb);
       __syncthreads();
       f32x16 sc[RB];         // scores S of one step
       bf16x8 pk[RB][2];      // probabilities P of one step (B operand of the PV MFMA)
-      float ms[RB];
       // S(j) in sc -> P(j) in pk: mask where the step is not full, raise the
-      // running max where needed, exponentiate
+      // running max where a score crossed the threshold, exponentiate
       auto softmax_step = [&](int j) {
-        const bool full = step_full(cx, j);
-        row_max<RB>(sc, sl2, ms);
-        if (!full) {
-          apply_mask(cx, j, rows, sc);
-          row_max<RB>(sc, sl2, ms);
+        if (!step_full(cx, j)) apply_mask(cx, j, rows, sc);
+        float mx[RB];
+        bool up = false;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          mx[rb] = lane_max(sc[rb]);
+          up |= mx[rb] > mst.thr[rb];
         }
-        raise_max<D, RB>(ms, m_run, lsum, o);
-        softmax_p<RB>(sc, sl2, m_run, pk);
+        if (__any(up)) raise_max<D, RB>(mx, mst, sc, lsum, o);
+        softmax_p<RB>(sc, pk, lsum);
       };
       // the work-group's share of the tile traffic of step s: rotate and store
-      // K(s+2), store V(s+1), issue the loads of K(s+3), V(s+2)
-      auto tiles = [&](int s) {
+      // K(s+2), store V(s+1) (stage st, loaded in step s-2), issue the loads
+      // of K(s+4), V(s+3) into the same stage
+      auto tiles = [&](int s, St& st) {
         store_k<D, RB, ROPE>(cx, s & 1, st);
         store_v<D, RB>(cx, (s + 1) & 1, st);
-        load_k<D, RB, ROPE>(cx, s + 3, st);
-        load_v<D, RB>(cx, s + 2, st);
+        load_k<D, RB, ROPE>(cx, s + kLoadAhead, st);
+        load_v<D, RB>(cx, s + kLoadAhead - 1, st);
       };
       // S(s+1) = K(s+1) Q^T and O += V(s) P(s), with the row sums of P(s)
       auto mfma = [&](int s) {
-        qk<D, RB>(cx, (s + 1) & 1, qf, sc);
-        pv<D, RB>(cx, s & 1, pk, o, lsum, ones);
-        sched_mfma<NKS + 2 * NDG, RB>();
+        qk<D, RB>(cx, (s + 1) & 1, qf, mst.bias, sc);
+        pv<D, RB>(cx, s & 1, pk, o);
       };
-      qk<D, RB>(cx, 0, qf, sc);
+      qk<D, RB>(cx, 0, qf, mst.bias, sc);
       if (lead) softmax_step(0);
       __syncthreads();   // K(0) read by every wave before step 0 reuses its buffer
 
@@ -594,21 +609,31 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
       // does the softmax of S(s) and the tile traffic first, then the MFMAs.
       // Both read K(s+1), V(s) and write K(s+2), V(s+1) (other buffers) in
       // step s; one barrier ends each step.
+      // The stages alternate with the step's parity, so the loop runs two
+      // steps per iteration.
+      auto lead_step = [&](int s, St& st) {
+        mfma(s);
+        __builtin_amdgcn_sched_barrier(0);
+        if (s + 1 < nsteps) softmax_step(s + 1);
+        tiles(s, st);
+        __syncthreads();
+      };
+      auto trail_step = [&](int s, St& st) {
+        softmax_step(s);
+        tiles(s, st);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma(s);
+        __syncthreads();
+      };
       if (lead) {
-        for (int s = 0; s < nsteps; ++s) {
-          mfma(s);
-          __builtin_amdgcn_sched_barrier(0);
-          if (s + 1 < nsteps) softmax_step(s + 1);
-          tiles(s);
-          __syncthreads();
+        for (int s = 0; s < nsteps; s += 2) {
+          lead_step(s, sa);
+          if (s + 1 < nsteps) lead_step(s + 1, sb);
         }
       } else {
-        for (int s = 0; s < nsteps; ++s) {
-          softmax_step(s);
-          tiles(s);
-          __builtin_amdgcn_sched_barrier(0);
-          mfma(s);
-          __syncthreads();
+        for (int s = 0; s < nsteps; s += 2) {
+          trail_step(s, sa);
+          if (s + 1 < nsteps) trail_step(s + 1, sb);
         }
       }
     }
@@ -616,7 +641,7 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
     // ---- epilogue
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const float l_tot = xor32_sum(h == 0 ? lsum[rb][0] : 0.f);
+      const float l_tot = xor32_sum(lsum[rb]);
       if (!rows.valid[rb]) continue;
       if (ns == 1) {
         __bf16* op = (__bf16*)P.out + qoff[rb];
@@ -641,7 +666,7 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
             const f32x4 u = {o[rb][dg][4 * j], o[rb][dg][4 * j + 1], o[rb][dg][4 * j + 2], o[rb][dg][4 * j + 3]};
             *(f32x4*)(po + 32 * dg + 8 * j + 4 * h) = u;
           }
-        if (h == 0) P.part_ml[pr] = make_float2(m_run[rb], l_tot);
+        if (h == 0) P.part_ml[pr] = make_float2(mst.m[rb], l_tot);
       }
     }
     if (tid == 0) s_next = resolve_ticket(P.hdr, s_qs, s_qc, q_cur, ticket);
