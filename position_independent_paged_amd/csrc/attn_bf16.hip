@@ -51,10 +51,11 @@ constexpr int kListMax = 256;     // list entries staged in LDS per pass
 // Sentinel entries after the last one of a pass (no block: loads return
 // zeros, never visible, never full), so the look-ups of the steps past the
 // end need no bounds test and the step body stays free of branches. Step s
-// issues the K loads of step s + 4 (entries 2s + 8, 2s + 9); with nsteps =
-// ceil(n / 2) the last index reached is n + 8.
+// issues the K loads of step s + 4 and reads the list entries of the loads of
+// step s + 1 (entries up to 2s + 11); with nsteps = ceil(n / 2) the last index
+// reached is n + 10.
 constexpr int kLoadAhead = 4;
-constexpr int kListPad = 2 * kLoadAhead + 2;
+constexpr int kListPad = 2 * kLoadAhead + 4;
 constexpr int kRsrcWord3 = 0x00020000;  // buffer descriptor word 3 (gfx9, raw dword access)
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -138,17 +139,37 @@ struct RowInfo {
   bool valid[RB], pdep[RB];
 };
 
-// physical block of list entry e (uniform; -1 for a sentinel past the list)
+// List look-ups of one step's tile loads, read from LDS a step before the
+// loads are issued (so no step waits on an LDS round trip for them): the
+// physical block of the wave's K block and of each of its V pieces (uniform
+// values, -1 past the list), and the logical position of the thread's key.
 template <int D, int RB>
-__device__ __forceinline__ int entry_phys(const StepCtx<D, RB>& cx, int e) {
-  e = __builtin_amdgcn_readfirstlane(e);
-  return __builtin_amdgcn_readfirstlane(cx.lst[e].phys);
+struct Pre {
+  int ph_k, pos;
+  int ph_v[Cfg<D, RB>::VU];
+};
+
+template <int D, int RB, bool ROPE>
+__device__ __forceinline__ void prefetch(const StepCtx<D, RB>& cx, int jk, int jv, Pre<D, RB>& pr) {
+  using C = Cfg<D, RB>;
+  const int tid = threadIdx.x;
+  const int t0 = __builtin_amdgcn_readfirstlane(tid);
+  const int ek = __builtin_amdgcn_readfirstlane(2 * jk + t0 / (C::KCH * kBlock));
+  pr.ph_k = cx.lst[ek].phys;
+  if (ROPE) pr.pos = cx.pos_s[ek * kBlock + (tid / C::KCH) % kBlock];
+#pragma unroll
+  for (int u = 0; u < C::VU; ++u) {
+    const int u0 = __builtin_amdgcn_readfirstlane(tid + u * C::NT);
+    const bool act = (C::VU * C::NT == C::VUNITS) || u0 < C::VUNITS;
+    pr.ph_v[u] = act ? cx.lst[__builtin_amdgcn_readfirstlane(2 * jv + u0 / (2 * D))].phys : -1;
+  }
 }
 
-// Global loads of step j's K unit and its cos/sin rows. Past the list or for
-// an invalid block the buffer is empty and the loads return zeros.
+// Global loads of a step's K unit and its cos/sin rows (list look-ups in
+// pr). Past the list or for an invalid block the buffer is empty and the
+// loads return zeros.
 template <int D, int RB, bool ROPE>
-__device__ __forceinline__ void load_k(const StepCtx<D, RB>& cx, int j, Stage<D, RB>& st) {
+__device__ __forceinline__ void load_k(const StepCtx<D, RB>& cx, const Pre<D, RB>& pr, Stage<D, RB>& st) {
   using C = Cfg<D, RB>;
   constexpr int CW = C::CW;
   const int tid = threadIdx.x;
@@ -156,9 +177,8 @@ __device__ __forceinline__ void load_k(const StepCtx<D, RB>& cx, int j, Stage<D,
   // a wave's K units lie in one block and are all active or all idle: derive
   // both from the wave's first thread so the buffer descriptor is scalar
   const int t0 = __builtin_amdgcn_readfirstlane(tid);
-  const int e = 2 * j + t0 / (C::KCH * kBlock);
   const int off = key % kBlock;
-  const int ph = entry_phys(cx, e);
+  const int ph = __builtin_amdgcn_readfirstlane(pr.ph_k);
   const int bytes = (ph >= 0 && t0 < C::KUNITS) ? kBlock * D * 2 : 0;
   const rsrc_t r = make_rsrc(cx.kc + (int64_t)(ph < 0 ? 0 : ph) * cx.group, bytes);
   const int row_b = (off * D + CW * ch) * 2;
@@ -174,8 +194,7 @@ __device__ __forceinline__ void load_k(const StepCtx<D, RB>& cx, int j, Stage<D,
     for (int i = 0; i < 2; ++i) { st.ka[i] = a[i]; st.kb[i] = b[i]; }
   }
   if (ROPE) {
-    const int pos = cx.pos_s[e * kBlock + off];
-    const int tb = (pos * D + CW * ch) * 4;
+    const int tb = (pr.pos * D + CW * ch) * 4;
 #pragma unroll
     for (int q = 0; q < CW / 4; ++q) {
       const f32x4 cv = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(cx.tab, tb + 16 * q, 0, 0));
@@ -188,15 +207,13 @@ __device__ __forceinline__ void load_k(const StepCtx<D, RB>& cx, int j, Stage<D,
 }
 
 template <int D, int RB>
-__device__ __forceinline__ void load_v(const StepCtx<D, RB>& cx, int j, Stage<D, RB>& st) {
+__device__ __forceinline__ void load_v(const StepCtx<D, RB>& cx, const Pre<D, RB>& pr, Stage<D, RB>& st) {
   using C = Cfg<D, RB>;
 #pragma unroll
   for (int u = 0; u < C::VU; ++u) {
-    const int unit = threadIdx.x + u * C::NT;
-    const int u0 = __builtin_amdgcn_readfirstlane(unit);   // a wave's pieces share one block
+    const int unit = threadIdx.x + u * C::NT;   // a wave's pieces share one block
     const int rem = unit % (2 * D);
-    const bool act = (C::VU * C::NT == C::VUNITS) || u0 < C::VUNITS;
-    const int ph = act ? entry_phys(cx, 2 * j + u0 / (2 * D)) : -1;
+    const int ph = __builtin_amdgcn_readfirstlane(pr.ph_v[u]);
     const rsrc_t r = make_rsrc(cx.vc + (int64_t)(ph < 0 ? 0 : ph) * cx.group, ph >= 0 ? kBlock * D * 2 : 0);
     st.v[u] = __builtin_bit_cast(
         u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, ((rem / 2) * kBlock + 8 * (rem % 2)) * 2, 0, 0));
@@ -286,11 +303,17 @@ __device__ __forceinline__ void pv(const StepCtx<D, RB>& cx, int buf, const bf16
     }
 }
 
-// true when every row of the tile sees every key of step j (uniform)
+// Bit j: every row of the tile sees every key of step j. One bit per step of
+// a pass (at most 128), built once per pass by a ballot over the list.
 template <int D, int RB>
-__device__ __forceinline__ bool step_full(const StepCtx<D, RB>& cx, int j) {
-  const int e = 2 * j;
-  return __builtin_amdgcn_readfirstlane(cx.lst[e].full & cx.lst[e + 1].full) != 0;
+__device__ __forceinline__ void full_steps(const StepCtx<D, RB>& cx, int nsteps, uint64_t (&fm)[2]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int j = 64 * h + lane;
+    const bool f = j < nsteps && (cx.lst[2 * j].full & cx.lst[2 * j + 1].full) != 0;
+    fm[h] = __ballot(f);
+  }
 }
 
 // element-wise mask of step j: block visibility and the causal diagonal
@@ -557,23 +580,31 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
       // in flight. Step s stores the stage it loaded two steps before, so each
       // load has two steps to arrive.
       St sa, sb;
-      load_k<D, RB, ROPE>(cx, 0, sa);
-      load_v<D, RB>(cx, 0, sa);
-      load_k<D, RB, ROPE>(cx, 1, sb);
+      Pre<D, RB> pr;
+      prefetch<D, RB, ROPE>(cx, 0, 0, pr);
+      load_k<D, RB, ROPE>(cx, pr, sa);
+      load_v<D, RB>(cx, pr, sa);
+      prefetch<D, RB, ROPE>(cx, 1, 1, pr);
+      load_k<D, RB, ROPE>(cx, pr, sb);
       store_k<D, RB, ROPE>(cx, 0, sa);
       store_v<D, RB>(cx, 0, sa);
-      load_k<D, RB, ROPE>(cx, 2, sa);
-      load_v<D, RB>(cx, 1, sa);
+      prefetch<D, RB, ROPE>(cx, 2, 1, pr);
+      load_k<D, RB, ROPE>(cx, pr, sa);
+      load_v<D, RB>(cx, pr, sa);
       store_k<D, RB, ROPE>(cx, 1, sb);
-      load_k<D, RB, ROPE>(cx, 3, sb);
-      load_v<D, RB>(cx, 2, sb);
+      prefetch<D, RB, ROPE>(cx, 3, 2, pr);
+      load_k<D, RB, ROPE>(cx, pr, sb);
+      load_v<D, RB>(cx, pr, sb);
+      prefetch<D, RB, ROPE>(cx, kLoadAhead, kLoadAhead - 1, pr);   // the loads of step 0
+      uint64_t fm[2];
+      full_steps(cx, nsteps, fm);
       __syncthreads();
       f32x16 sc[RB];         // scores S of one step
       bf16x8 pk[RB][2];      // probabilities P of one step (B operand of the PV MFMA)
       // S(j) in sc -> P(j) in pk: mask where the step is not full, raise the
       // running max where a score crossed the threshold, exponentiate
       auto softmax_step = [&](int j) {
-        if (!step_full(cx, j)) apply_mask(cx, j, rows, sc);
+        if ((((j < 64 ? fm[0] : fm[1]) >> (j & 63)) & 1) == 0) apply_mask(cx, j, rows, sc);
         float mx[RB];
         bool up = false;
 #pragma unroll
@@ -586,12 +617,14 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
       };
       // the work-group's share of the tile traffic of step s: rotate and store
       // K(s+2), store V(s+1) (stage st, loaded in step s-2), issue the loads
-      // of K(s+4), V(s+3) into the same stage
+      // of K(s+4), V(s+3) into the same stage, read the list entries of the
+      // next step's loads
       auto tiles = [&](int s, St& st) {
         store_k<D, RB, ROPE>(cx, s & 1, st);
         store_v<D, RB>(cx, (s + 1) & 1, st);
-        load_k<D, RB, ROPE>(cx, s + kLoadAhead, st);
-        load_v<D, RB>(cx, s + kLoadAhead - 1, st);
+        load_k<D, RB, ROPE>(cx, pr, st);
+        load_v<D, RB>(cx, pr, st);
+        prefetch<D, RB, ROPE>(cx, s + 1 + kLoadAhead, s + kLoadAhead, pr);
       };
       // S(s+1) = K(s+1) Q^T and O += V(s) P(s), with the row sums of P(s)
       auto mfma = [&](int s) {
