@@ -640,13 +640,15 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
       // ALU work: a leading wave does the MFMA part of step s first, then the
       // softmax of S(s+1) and its share of the tile traffic; a trailing wave
       // does the softmax of S(s) and the tile traffic first, then the MFMAs.
+      // (This is program order: the compiler is free to interleave the
+      // independent instructions of the parts, which measured faster than
+      // fencing them.)
       // Both read K(s+1), V(s) and write K(s+2), V(s+1) (other buffers) in
       // step s; one barrier ends each step.
       // The stages alternate with the step's parity, so the loop runs two
       // steps per iteration.
       auto lead_step = [&](int s, St& st) {
         mfma(s);
-        __builtin_amdgcn_sched_barrier(0);
         if (s + 1 < nsteps) softmax_step(s + 1);
         tiles(s, st);
         __syncthreads();
@@ -654,7 +656,6 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
       auto trail_step = [&](int s, St& st) {
         softmax_step(s);
         tiles(s, st);
-        __builtin_amdgcn_sched_barrier(0);
         mfma(s);
         __syncthreads();
       };
