@@ -56,6 +56,7 @@ constexpr int kListMax = 256;     // list entries staged in LDS per pass
 // reached is n + 10.
 constexpr int kLoadAhead = 4;
 constexpr int kListPad = 2 * kLoadAhead + 4;
+constexpr int kClaimLate = -2;   // s_next: the claimed ticket is past its queue
 constexpr int kRsrcWord3 = 0x00020000;  // buffer descriptor word 3 (gfx9, raw dword access)
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -407,6 +408,23 @@ __device__ __forceinline__ void raise_max(const float (&mx)[RB], MaxState<RB>& m
   }
 }
 
+// Work item i through the constant address space: with a uniform index the
+// fields arrive by scalar loads (the list was written by an earlier launch).
+__device__ __forceinline__ Item load_item(const Item* items, int i) {
+  typedef const __attribute__((address_space(4))) int32_t CI;
+  const CI* f = (const CI*)(items + i);
+  Item t;
+  t.tile = f[0];
+  t.p0 = f[1];
+  t.p1 = f[2];
+  t.gsn = (uint32_t)f[3];
+  t.r = f[4];
+  t.row0 = f[5];
+  t.nq = f[6];
+  t.slot0 = f[7];
+  return t;
+}
+
 template <int D, int G, bool ROPE, int RB>
 __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams P) {
   using C = Cfg<D, RB>;
@@ -415,9 +433,9 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
   constexpr int BQ = C::ROWS / G;
   constexpr int NKS = D / 16;             // k-steps of QK^T
   constexpr int NDG = D / 32;             // 32-row d blocks of O^T
-  __shared__ BlkDesc lst[kListMax + kListPad];
-  __shared__ int pos_s[ROPE ? (kListMax + kListPad) * kBlock : 1];
-  __shared__ int s_next;
+  __shared__ __attribute__((aligned(16))) BlkDesc lst[kListMax + kListPad];
+  __shared__ __attribute__((aligned(16))) int pos_s[ROPE ? (kListMax + kListPad) * kBlock : 4];
+  __shared__ int s_first, s_next, s_late;
   __shared__ uint32_t s_qs[kQueues], s_qc[kQueues];
   __shared__ __attribute__((aligned(16))) __bf16 kl[2 * C::KSZ];
   __shared__ __attribute__((aligned(16))) __bf16 vl[2 * C::VSZ];
@@ -441,19 +459,81 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
   }
   int q_cur = blockIdx.x % kQueues;   // queue being drained (thread 0)
   __syncthreads();
-  if (tid == 0) s_next = resolve_ticket(P.hdr, s_qs, s_qc, q_cur, atomicAdd(&P.hdr->next[q_cur], 1u));
+  if (tid == 0) s_first = resolve_ticket(P.hdr, s_qs, s_qc, q_cur, atomicAdd(&P.hdr->next[q_cur], 1u));
   __syncthreads();
-  int it = __builtin_amdgcn_readfirstlane(s_next);
+  int it = __builtin_amdgcn_readfirstlane(s_first);
+  Item item{};
+  if (it >= 0) item = load_item(P.items, it);
   while (it >= 0) {
-    uint32_t ticket = 0;   // claim of the following item, checked when this one ends
+    // Claim the following item now. Thread 0 resolves the ticket once the
+    // rows below are in (the atomic has returned by then) when it falls
+    // inside the current queue, and every wave reads s_next after the first
+    // staging barrier; s_next is written again only after this item's step
+    // barriers, so the item needs no barrier at its end, and the following
+    // item's fields are read during this one (scalar loads). A ticket past
+    // its queue is resolved at the end of the item (the queue walk, with a
+    // barrier), off the critical path of the item.
+    uint32_t ticket = 0;
     if (tid == 0) ticket = atomicAdd(&P.hdr->next[q_cur], 1u);
-    const Item item = P.items[it];
+    int nxt = -1;
+    Item nitem = item;
     const int g = item.gsn & 0xff;
     const int sp = (item.gsn >> 8) & 0xfff;
     const int ns = item.gsn >> 20;
     const int32_t* lpos = P.logical_pos + (int64_t)item.r * P.max_blocks * kBlock;
     const BlkDesc* blist = P.blist + (int64_t)item.tile * P.max_blocks;
     const int64_t kv_head = (int64_t)g * kBlock * D;   // offset of head g inside a block group
+
+    // ---- the list of the first pass is fetched before the rows, so that its
+    // loads and those of q are in flight together
+    // (entries past the piece are sentinels: above every query block, so
+    // never visible, no block, never full)
+    constexpr int LI = (kListMax + kListPad + NT - 1) / NT;
+    u32x4 bdv[LI][2];
+    auto fetch_list = [&](int c0, int n_l) {
+#pragma unroll
+      for (int k = 0; k < LI; ++k) {
+        const int i = tid + k * NT;
+        const u32x4* src = (const u32x4*)(blist + c0 + (i < n_l ? i : 0));
+        bdv[k][0] = i < n_l ? src[0] : u32x4{1u << 26, 0xffffffffu, 0xffffffffu, 0u};
+        bdv[k][1] = i < n_l ? src[1] : u32x4{0u, 0u, 0u, 0u};
+      }
+    };
+    // The thread that holds entry i also writes the logical positions of its
+    // 16 keys: its base position plus the key offset, or (positions that do
+    // not run consecutively) the request's positions, clamped to the table.
+    auto store_list = [&](int n_l) {
+#pragma unroll
+      for (int k = 0; k < LI; ++k) {
+        const int i = tid + k * NT;
+        if (i < n_l + kListPad) {
+          u32x4* dst = (u32x4*)(lst + i);
+          dst[0] = bdv[k][0];
+          dst[1] = bdv[k][1];
+          if (ROPE) {
+            const int kb = (int)bdv[k][0][0];
+            const int pos0 = (int)bdv[k][1][0];
+            u32x4* pd = (u32x4*)(pos_s + i * kBlock);
+            if (pos0 >= 0) {
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                pd[q] = u32x4{(uint32_t)(pos0 + 4 * q), (uint32_t)(pos0 + 4 * q + 1), (uint32_t)(pos0 + 4 * q + 2),
+                              (uint32_t)(pos0 + 4 * q + 3)};
+            } else {
+              for (int o2 = 0; o2 < kBlock; ++o2) {
+                int pos = lpos[kb * kBlock + o2];
+                if (pos < 0 || pos >= P.max_pos) {
+                  atomicOr(&P.hdr->err, (uint32_t)MINIPIC_EW_POS);
+                  pos = pos < 0 ? 0 : P.max_pos - 1;
+                }
+                pos_s[i * kBlock + o2] = pos;
+              }
+            }
+          }
+        }
+      }
+    };
+    fetch_list(item.p0, min(kListMax, item.p1 - item.p0));
 
     // ---- the lane's query rows
     RowInfo<RB> rows;
@@ -475,6 +555,11 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
       const __bf16* qp = (const __bf16*)P.q + qoff[rb];
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) qf[rb][ks] = valid ? *(const bf16x8*)(qp + 16 * ks + 8 * h) : bf16x8{};
+    }
+    store_list(min(kListMax, item.p1 - item.p0));
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      const bool valid = rows.valid[rb];
       // q is scaled by scale * log2(e) here, so that the MFMA gives the scores in
       // log2 units (rounded to bf16 once with the rotation below)
       if (!(P.flags & MINIPIC_FLAG_ROTATE_Q)) {
@@ -486,7 +571,7 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
           qf[rb][ks] = __builtin_bit_cast(bf16x8, u);
         }
       } else if (valid) {
-        int pos = lpos[tk.c];
+        int pos = lpos[rows.c[rb]];
         if (pos < 0 || pos >= P.max_pos) {
           atomicOr(&P.hdr->err, (uint32_t)MINIPIC_EW_POS);
           pos = pos < 0 ? 0 : P.max_pos - 1;
@@ -513,6 +598,8 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
       }
     }
 
+    if (tid == 0) s_next = ticket < s_qc[q_cur] ? (int)(s_qs[q_cur] + ticket) : kClaimLate;
+
     f32x16 o[RB][NDG];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
@@ -531,38 +618,16 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
     for (int c0 = item.p0; c0 < item.p1; c0 += kListMax) {
       const int n_l = min(kListMax, item.p1 - c0);
       const int nsteps = (n_l + 1) / 2;
-      // ---- stage the list piece and the keys' logical positions (read from
-      // the list in global memory, so one barrier covers both)
-      for (int i = tid; i < n_l + kListPad; i += NT) {
-        BlkDesc bd;
-        if (i < n_l) {
-          bd = blist[c0 + i];
-        } else {
-          bd.kb = 1 << 26;   // above every query block: never visible
-          bd.phys = -1;
-          bd.span = -1;
-          bd.flags = 0;
-          bd.pos0 = 0;
-          bd.full = 0;
-        }
-        lst[i] = bd;
-      }
-      if (ROPE) {
-        for (int i = tid; i < (n_l + kListPad) * kBlock; i += NT) {
-          int pos = 0;
-          if (i < n_l * kBlock) {
-            const BlkDesc* bd = blist + c0 + i / kBlock;
-            const int pos0 = bd->pos0;
-            pos = pos0 >= 0 ? pos0 + i % kBlock : lpos[bd->kb * kBlock + i % kBlock];
-            if (pos < 0 || pos >= P.max_pos) {
-              atomicOr(&P.hdr->err, (uint32_t)MINIPIC_EW_POS);
-              pos = pos < 0 ? 0 : P.max_pos - 1;
-            }
-          }
-          pos_s[i] = pos;
-        }
+      // ---- stage the list piece (the first pass was staged with the rows)
+      if (c0 != item.p0) {
+        fetch_list(c0, n_l);
+        store_list(n_l);
       }
       __syncthreads();
+      if (c0 == item.p0) {
+        nxt = __builtin_amdgcn_readfirstlane(s_next);
+        if (nxt >= 0) nitem = load_item(P.items, nxt);
+      }
 
       StepCtx<D, RB> cx;
       cx.lst = lst;
@@ -703,10 +768,14 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
         if (h == 0) P.part_ml[pr] = make_float2(mst.m[rb], l_tot);
       }
     }
-    if (tid == 0) s_next = resolve_ticket(P.hdr, s_qs, s_qc, q_cur, ticket);
-    __syncthreads();
-    // s_next is written again only after the next item's barriers
-    it = __builtin_amdgcn_readfirstlane(s_next);
+    if (nxt == kClaimLate) {
+      if (tid == 0) s_late = resolve_ticket(P.hdr, s_qs, s_qc, q_cur, ticket);
+      __syncthreads();
+      nxt = __builtin_amdgcn_readfirstlane(s_late);
+      if (nxt >= 0) nitem = load_item(P.items, nxt);
+    }
+    it = nxt;
+    item = nitem;
   }
 }
 

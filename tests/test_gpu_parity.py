@@ -240,6 +240,31 @@ def test_shifted_positions():
     check("shift6000", got, want, "bf16")
 
 
+@pytest.mark.parametrize("flags", ["rotate_q", "prerotated_q"])
+def test_nonconsecutive_positions(flags):
+    """Logical positions that do not run consecutively inside a block (every
+    other block reversed, some far from the context index): those blocks take
+    the per-key position look-up instead of the block's base position."""
+    import position_independent_paged_amd as pip
+    w0 = _variant("bf16", 4, 128, seed=11)
+    pos = []
+    for r, L in enumerate(w0.ctx_len):
+        p_ = np.arange(int(L), dtype=np.int32)
+        for b0 in range(0, int(L), 32):                     # reverse the positions of every other block
+            blk = p_[b0:b0 + 16]
+            p_[b0:b0 + len(blk)] = blk[::-1] + 3000 * (r + 1)
+        pos.append(p_)
+    w = workload.custom("v", w0.segments, pool_lengths=[32, 48], num_q_heads=8, num_kv_heads=2, head_dim=128,
+                        dtype="bf16", rope_theta=5e5, max_pos=8192, seed=11, positions=pos)
+    say(f"non-consecutive positions ({flags}) ctx={list(w.ctx_len)}")
+    dw = stage(w, flags=pip.MINIPIC_FLAG_ROTATE_Q if flags == "rotate_q" else 0)
+    dw.step()
+    torch.cuda.synchronize()
+    assert dw.error_word() == 0
+    got, want = compare_workload(w, out_f64(dw.out), q_rotated=flags != "rotate_q")
+    check(f"nonconsecutive/{flags}", got, want, "bf16")
+
+
 def test_edge_layouts():
     """A request with no query rows, one single-token request, the same pool
     span twice in one request, queries that are not a suffix, and a ragged
