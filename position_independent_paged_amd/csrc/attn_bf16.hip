@@ -544,6 +544,14 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
     for (int rb = 0; rb < RB; ++rb) {
       row[rb] = 32 * RB * w + 32 * rb + l32;
       const int tok = row[rb] / G;
+      // q of a row past the tile's end is read from its last token (an
+      // address inside q) and zeroed below, so the load does not wait for
+      // the row's descriptor
+      const int tok_in = tok < item.nq ? tok : item.nq - 1;
+      qoff[rb] = (((int64_t)item.row0 + tok_in) * P.hq + g * G + row[rb] % G) * D;
+      const __bf16* qp = (const __bf16*)P.q + qoff[rb];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) qf[rb][ks] = *(const bf16x8*)(qp + 16 * ks + 8 * h);
       const TokDesc tk = P.toks[(int64_t)item.tile * BQ + tok];
       const bool valid = tok < item.nq && tk.c >= 0;
       rows.valid[rb] = valid;
@@ -551,15 +559,15 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
       rows.bq[rb] = valid ? (tk.c >> 4) : -1;
       rows.span[rb] = tk.span;
       rows.pdep[rb] = valid && tk.pdep;
-      qoff[rb] = (((int64_t)item.row0 + tok) * P.hq + g * G + row[rb] % G) * D;
-      const __bf16* qp = (const __bf16*)P.q + qoff[rb];
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) qf[rb][ks] = valid ? *(const bf16x8*)(qp + 16 * ks + 8 * h) : bf16x8{};
     }
     store_list(min(kListMax, item.p1 - item.p0));
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const bool valid = rows.valid[rb];
+      if (!valid) {
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) qf[rb][ks] = bf16x8{};
+      }
       // q is scaled by scale * log2(e) here, so that the MFMA gives the scores in
       // log2 units (rounded to bf16 once with the rotation below)
       if (!(P.flags & MINIPIC_FLAG_ROTATE_Q)) {

@@ -47,6 +47,7 @@ typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
 constexpr int kBlock = 16;        // tokens per cache block
 constexpr int kMaxSplits = 64;    // key-list pieces per tile at most
 constexpr int kCostBins = 1024;   // item sort buckets (cost in key blocks, clipped)
+constexpr int kItemCostBlocks = 16;  // fixed cost of starting a work item, in key blocks
 constexpr int kPlanThreads = 1024;// plan_tiles work-group size
 constexpr int kPlanBlocksPerThread = 2;  // key blocks per plan_tiles thread and pass
 constexpr int kTileCache = 4096;  // tiles whose list lengths plan_items keeps in LDS

@@ -60,7 +60,7 @@ struct Plan {
 };
 
 constexpr size_t kAlign = 256;
-constexpr int kSlotCap = 512;   // partial-result slots: about two pieces per CU of a 256-CU GPU
+constexpr int kSlotCap = 512;   // partial-result slots: room for two pieces per CU of a 256-CU GPU
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 int check_batch(const minipic_batch* b, int dtype) {

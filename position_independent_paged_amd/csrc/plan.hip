@@ -262,13 +262,16 @@ __global__ void __launch_bounds__(kItemThreads) plan_items_kernel(PlanParams P) 
   __syncthreads();
   auto nlist = [&](int t) { return t < kTileCache ? s_nl[t] : P.tiles[t].nlist; };
 
-  // ---- piece length: about two pieces of work per persistent work-group,
+  // ---- piece length: about one piece of work per persistent work-group,
   // never shorter than min_chunk, and few enough split tiles to fit the
-  // partial-result slots
+  // partial-result slots. The work of a tile counts its key blocks plus the
+  // fixed cost of starting an item (staging its list and query rows, filling
+  // the load pipeline, storing its result), so pieces of long lists come out
+  // longer where many short tiles share the grid.
   long long work = 0;
-  for (int t = tid; t < T; t += NT) work += nlist(t);
+  for (int t = tid; t < T; t += NT) work += nlist(t) > 0 ? nlist(t) + kItemCostBlocks : 0;
   work = block_sum_ll<NT>(work, red) * H;
-  const long long per = 2LL * P.num_wg;
+  const long long per = P.num_wg;
   long long cl = (work + per - 1) / per;
   int chunk = (int)(cl < (long long)P.min_chunk ? P.min_chunk : (cl > (1LL << 30) ? (1LL << 30) : cl));
   for (int iter = 0; iter < 40; ++iter) {
