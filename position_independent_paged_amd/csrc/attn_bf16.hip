@@ -439,6 +439,11 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
   __shared__ uint32_t s_qs[kQueues], s_qc[kQueues];
   __shared__ __attribute__((aligned(16))) __bf16 kl[2 * C::KSZ];
   __shared__ __attribute__((aligned(16))) __bf16 vl[2 * C::VSZ];
+  // the query rows of the work item, bf16, one padded row each: q passes
+  // through it on the way in and the normalised output on the way out, so
+  // that every global load or store instruction moves whole rows (each
+  // wave uses only its own rows)
+  __shared__ __attribute__((aligned(16))) __bf16 rowbuf[C::ROWS * C::KSTR];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -465,16 +470,16 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
   Item item{};
   if (it >= 0) item = load_item(P.items, it);
   while (it >= 0) {
-    // Claim the following item now. Thread 0 resolves the ticket once the
-    // rows below are in (the atomic has returned by then) when it falls
-    // inside the current queue, and every wave reads s_next after the first
-    // staging barrier; s_next is written again only after this item's step
-    // barriers, so the item needs no barrier at its end, and the following
-    // item's fields are read during this one (scalar loads). A ticket past
-    // its queue is resolved at the end of the item (the queue walk, with a
-    // barrier), off the critical path of the item.
+    // Claim the following item now. Thread 0 publishes the ticket's item
+    // (when it falls inside the current queue) just before the prologue's
+    // first barrier, long after the atomic has returned, and every wave reads
+    // s_next after the prologue's second barrier; s_next is written again
+    // only in the next item's prologue, after that item's staging barrier, so
+    // the item needs no barrier at its end, and the following item's fields
+    // are read during this one (scalar loads). A ticket past its queue is
+    // resolved at the end of the item (the queue walk, with a barrier), off
+    // the critical path of the item.
     uint32_t ticket = 0;
-    if (tid == 0) ticket = atomicAdd(&P.hdr->next[q_cur], 1u);
     int nxt = -1;
     Item nitem = item;
     const int g = item.gsn & 0xff;
@@ -538,20 +543,42 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
     // ---- the lane's query rows
     RowInfo<RB> rows;
     int row[RB];
-    int64_t qoff[RB];
     bf16x8 qf[RB][NKS];
+    // q rows of the wave: lane i loads 16-byte piece i % CPR of row i / CPR
+    // (+ RPI per round), so a load instruction reads RPI whole rows; they go
+    // to the wave's rows of rowbuf. A row past the tile's end is read from
+    // its last token (an address inside q) and zeroed below, so the loads do
+    // not wait for the row descriptors.
+    constexpr int CPR = D / 8;          // 16-byte pieces per row
+    constexpr int RPI = 64 / CPR;       // rows per load instruction
+    constexpr int QLD = 32 * RB / RPI;  // load instructions per lane
+    constexpr int QGR = QLD < 4 ? QLD : 4;  // of them in flight together
+    // (the lane index is made opaque here so that the row addresses, the
+    // same for every item, are computed when used instead of being kept in
+    // registers across the item loop)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int k0 = 0; k0 < QLD; k0 += QGR) {
+      u32x4 qv[QGR];
+#pragma unroll
+      for (int k = 0; k < QGR; ++k) {
+        const int rw = 32 * RB * w + RPI * (k0 + k) + ln / CPR;
+        const int tq = rw / G;
+        const int tq_in = tq < item.nq ? tq : item.nq - 1;
+        qv[k] = *(const u32x4*)((const __bf16*)P.q + (((int64_t)item.row0 + tq_in) * P.hq + g * G + rw % G) * D +
+                                8 * (ln % CPR));
+      }
+#pragma unroll
+      for (int k = 0; k < QGR; ++k)
+        *(u32x4*)(rowbuf + (32 * RB * w + RPI * (k0 + k) + ln / CPR) * C::KSTR + 8 * (ln % CPR)) = qv[k];
+    }
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       row[rb] = 32 * RB * w + 32 * rb + l32;
       const int tok = row[rb] / G;
-      // q of a row past the tile's end is read from its last token (an
-      // address inside q) and zeroed below, so the load does not wait for
-      // the row's descriptor
-      const int tok_in = tok < item.nq ? tok : item.nq - 1;
-      qoff[rb] = (((int64_t)item.row0 + tok_in) * P.hq + g * G + row[rb] % G) * D;
-      const __bf16* qp = (const __bf16*)P.q + qoff[rb];
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) qf[rb][ks] = *(const bf16x8*)(qp + 16 * ks + 8 * h);
+      for (int ks = 0; ks < NKS; ++ks) qf[rb][ks] = *(const bf16x8*)(rowbuf + row[rb] * C::KSTR + 16 * ks + 8 * h);
       const TokDesc tk = P.toks[(int64_t)item.tile * BQ + tok];
       const bool valid = tok < item.nq && tk.c >= 0;
       rows.valid[rb] = valid;
@@ -560,6 +587,9 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
       rows.span[rb] = tk.span;
       rows.pdep[rb] = valid && tk.pdep;
     }
+    // the claim is issued after the list and q loads: loads retire in issue
+    // order, so the waits for them do not wait for the atomic as well
+    if (tid == 0) ticket = atomicAdd(&P.hdr->next[q_cur], 1u);
     store_list(min(kListMax, item.p1 - item.p0));
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -606,7 +636,6 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
       }
     }
 
-    if (tid == 0) s_next = ticket < s_qc[q_cur] ? (int)(s_qs[q_cur] + ticket) : kClaimLate;
 
     f32x16 o[RB][NDG];
 #pragma unroll
@@ -632,10 +661,6 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
         store_list(n_l);
       }
       __syncthreads();
-      if (c0 == item.p0) {
-        nxt = __builtin_amdgcn_readfirstlane(s_next);
-        if (nxt >= 0) nitem = load_item(P.items, nxt);
-      }
 
       StepCtx<D, RB> cx;
       cx.lst = lst;
@@ -671,6 +696,7 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
       prefetch<D, RB, ROPE>(cx, kLoadAhead, kLoadAhead - 1, pr);   // the loads of step 0
       uint64_t fm[2];
       full_steps(cx, nsteps, fm);
+      if (c0 == item.p0 && tid == 0) s_next = ticket < s_qc[q_cur] ? (int)(s_qs[q_cur] + ticket) : kClaimLate;
       __syncthreads();
       f32x16 sc[RB];         // scores S of one step
       bf16x8 pk[RB][2];      // probabilities P of one step (B operand of the PV MFMA)
@@ -707,6 +733,10 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
       qk<D, RB>(cx, 0, qf, mst.bias, sc);
       if (lead) softmax_step(0);
       __syncthreads();   // K(0) read by every wave before step 0 reuses its buffer
+      if (c0 == item.p0) {
+        nxt = __builtin_amdgcn_readfirstlane(s_next);
+        if (nxt >= 0) nitem = load_item(P.items, nxt);
+      }
 
       // Steps. The two waves sharing a SIMD work in opposite order inside a
       // step, so that one issues its MFMAs while the other runs its vector
@@ -746,13 +776,16 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
     }
 
     // ---- epilogue
+    if (ns == 1) {
+      // out = O / l in bf16: the wave's rows go to rowbuf, then every store
+      // instruction writes RPI whole rows of out (rows past the tile's end
+      // or without keys are not written)
+      uint32_t vmask[RB];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      const float l_tot = xor32_sum(lsum[rb]);
-      if (!rows.valid[rb]) continue;
-      if (ns == 1) {
-        __bf16* op = (__bf16*)P.out + qoff[rb];
-        const float inv = 1.f / l_tot;
+      for (int rb = 0; rb < RB; ++rb) {
+        const float inv = 1.f / xor32_sum(lsum[rb]);
+        vmask[rb] = (uint32_t)__ballot(rows.valid[rb]);
+        __bf16* rp = rowbuf + row[rb] * C::KSTR + 4 * h;
 #pragma unroll
         for (int dg = 0; dg < NDG; ++dg)
 #pragma unroll
@@ -760,20 +793,39 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
             u32x2 u;
             u[0] = pack_bf16x2(o[rb][dg][4 * j] * inv, o[rb][dg][4 * j + 1] * inv);
             u[1] = pack_bf16x2(o[rb][dg][4 * j + 2] * inv, o[rb][dg][4 * j + 3] * inv);
-            *(u32x2*)(op + 32 * dg + 8 * j + 4 * h) = u;
+            *(u32x2*)(rp + 32 * dg + 8 * j) = u;
           }
-      } else {
-        // a piece of a split tile: fp32 partial result to its slot (merged by merge_kernel)
-        const int64_t pr = (int64_t)(item.slot0 + g * ns + sp) * C::ROWS + row[rb];
-        float* po = P.part_o + pr * D;
+      }
+      int ln = lane;   // opaque: see the q staging
+      asm volatile("" : "+v"(ln));
+#pragma unroll
+      for (int k = 0; k < 32 * RB / RPI; ++k) {
+        const int rr = RPI * k + ln / CPR;   // row within the wave's rows
+        const u32x4 v = *(const u32x4*)(rowbuf + (32 * RB * w + rr) * C::KSTR + 8 * (ln % CPR));
+        if ((vmask[rr / 32] >> (rr % 32)) & 1u) {
+          const int rw = 32 * RB * w + rr;
+          *(u32x4*)((__bf16*)P.out + (((int64_t)item.row0 + rw / G) * P.hq + g * G + rw % G) * D +
+                    8 * (ln % CPR)) = v;
+        }
+      }
+    } else {
+      // a piece of a split tile: fp32 (O, m, l) to its slot, merged by
+      // merge_kernel. O is stored in the lanes' own order: the 32-row block
+      // of a wave is [d/32][(d%32)/8][lane][4] with lane = row + 32 ((d%8)/4),
+      // so every store instruction writes 1 KiB in one piece.
+      const int slot = item.slot0 + g * ns + sp;
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const float l_tot = xor32_sum(lsum[rb]);
+        float* po = P.part_o + ((int64_t)slot * C::ROWS + 32 * (RB * w + rb)) * D + 4 * lane;
 #pragma unroll
         for (int dg = 0; dg < NDG; ++dg)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const f32x4 u = {o[rb][dg][4 * j], o[rb][dg][4 * j + 1], o[rb][dg][4 * j + 2], o[rb][dg][4 * j + 3]};
-            *(f32x4*)(po + 32 * dg + 8 * j + 4 * h) = u;
+            *(f32x4*)(po + (dg * 4 + j) * 256) = u;
           }
-        if (h == 0) P.part_ml[pr] = make_float2(mst.m[rb], l_tot);
+        if (h == 0 && rows.valid[rb]) P.part_ml[(int64_t)slot * C::ROWS + row[rb]] = make_float2(mst.m[rb], l_tot);
       }
     }
     if (nxt == kClaimLate) {

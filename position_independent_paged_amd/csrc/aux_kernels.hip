@@ -176,7 +176,16 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnParams P, int G) {
     __syncthreads();
 
     if (valid) {
-      const float* po = P.part_o + base * D + 4 * d4;
+      // elements d .. d+3 of the row in piece 0: the bf16 attention kernel
+      // stores each 32-row block in its lanes' order ([d/32][(d%32)/8][lane][4],
+      // lane = row % 32 + 32 ((d%8)/4)); the fp32 kernel stores plain rows
+      const float* po;
+      if constexpr (sizeof(T) == 2) {
+        const int dg = d4 / 8, j = (d4 / 2) % 4, hh = d4 % 2;
+        po = P.part_o + ((int64_t)grp.slot0 * ROWS + (row & ~31)) * D + ((dg * 4 + j) * 64 + (row & 31) + 32 * hh) * 4;
+      } else {
+        po = P.part_o + base * D + 4 * d4;
+      }
       f32x4 num = {0.f, 0.f, 0.f, 0.f};
       for (int s0 = 0; s0 < ns; s0 += UNR) {
         f32x4 v[UNR];

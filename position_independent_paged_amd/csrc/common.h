@@ -177,7 +177,7 @@ struct AttnParams {
   const Item* items;
   const Group* groups;
   float2* part_ml;     // [slots][rows] (m in log2 units, l)
-  float* part_o;       // [slots][rows][D]
+  float* part_o;       // [slots][rows][D]; the bf16 kernel orders each 32-row block by lane (see its epilogue)
   int32_t hq;
   int32_t hkv;
   int32_t max_blocks;
@@ -270,19 +270,30 @@ __device__ __forceinline__ bool block_visible(int kb, int span, int flags, int b
 
 // Work items are claimed with one atomic add on the counter of the queue the
 // work-group is draining, issued when the work-group starts an item; the
-// ticket is checked against the queue's size when that item ends, so the
+// ticket is checked against the queue's size later in that item, so the
 // claim's latency hides behind the item's work. A ticket past the end means
-// the queue is drained: the work-group moves on to the next queue (queues
-// never refill), and returns -1 when every queue is drained. `qs`, `qc` hold
-// the queues' first items and sizes (copied to LDS). Thread 0 only.
+// the queue is drained: the work-group moves on to the other queues (queues
+// never refill), and returns -1 when every queue is drained. The counters
+// only grow, so a queue whose counter already reads at or past its size is
+// empty for good: the counters of all queues are read in one round trip and
+// only a queue that may still hold items is claimed from. `qs`, `qc` hold the
+// queues' first items and sizes (copied to LDS). Thread 0 only.
 __device__ __forceinline__ int resolve_ticket(WsHeader* hdr, const uint32_t* qs, const uint32_t* qc, int& q,
                                               uint32_t ticket) {
-  for (int k = 0;; ++k) {
-    if (ticket < qc[q]) return (int)(qs[q] + ticket);
-    if (k + 1 >= kQueues) return -1;
-    q = (q + 1) % kQueues;
-    ticket = atomicAdd(&hdr->next[q], 1u);
+  if (ticket < qc[q]) return (int)(qs[q] + ticket);
+  uint32_t seen[kQueues];
+#pragma unroll
+  for (int k = 0; k < kQueues; ++k) seen[k] = __hip_atomic_load(&hdr->next[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int k = 1; k < kQueues; ++k) {
+    const int q2 = (q + k) % kQueues;
+    if (seen[q2] >= qc[q2]) continue;
+    const uint32_t t = atomicAdd(&hdr->next[q2], 1u);
+    if (t < qc[q2]) {
+      q = q2;
+      return (int)(qs[q2] + t);
+    }
   }
+  return -1;
 }
 
 }  // namespace minipic
