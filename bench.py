@@ -15,7 +15,9 @@ PDep suffix: 15,872 query tokens over a 31,232-token context.
 
 Prints ONE JSON line. `value` is query tokens per second of the whole step;
 the `roofline` object prices the attention kernel (its average launch
-duration from HIP events the library records around it on the launch stream)
+duration over a second pass of the same timed steps, from the HIP events the
+library records around its launches on the launch stream, read once after the
+last step)
 against the bf16 MFMA peak using the exact count of visible (query, key)
 pairs: FLOPs = 4 * d * Hq * pairs. Its `traffic` is the kernel's HBM bytes per
 launch from rocprofv3 FETCH_SIZE / WRITE_SIZE counters (scaled by what the
@@ -72,7 +74,7 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="c4", choices=sorted(k for k in WORKLOADS if k.startswith("c")))
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample (0 disables the cpu_baseline leg)")
@@ -220,18 +222,22 @@ def algorithmic_bytes(w):
     return qo + kv + cs
 
 
-def kernel_ms(call, reps):
-    """Average (plan, attention, merge) kernel durations of `call` from the library's HIP events."""
-    from position_independent_paged_amd import minipic_kernel_times, minipic_set_kernel_timing
+def steps_kernel_ms(step, n):
+    """Average (plan, attention, merge) kernel durations over n back-to-back calls of `step` (each making one
+    attention call), from the HIP events the library records around its launches, read after the last step."""
+    import torch
+    from position_independent_paged_amd import minipic_kernel_times_all, minipic_set_kernel_timing
+    torch.cuda.synchronize()
     minipic_set_kernel_timing(True)
-    acc = [0.0, 0.0, 0.0]
     try:
-        for _ in range(reps):
-            call()
-            acc = [x + y for x, y in zip(acc, minipic_kernel_times())]
+        for _ in range(n):
+            step()
+        times = minipic_kernel_times_all(n)
     finally:
         minipic_set_kernel_timing(False)
-    return [x / reps for x in acc]
+    if len(times) != n:
+        raise RuntimeError(f"{len(times)} timed calls, expected {n}")
+    return [sum(t[i] for t in times) / n for i in range(3)]
 
 
 def private_copy_prerotated(dw, w, reps):
@@ -260,7 +266,7 @@ def private_copy_prerotated(dw, w, reps):
         minipic_reference_prerotated(dw.q, k_priv, v_priv, len(src), batch.struct, dw.out, dw.workspace,
                                      cos_sin=dw.cos_sin, max_pos=dw.max_pos)
     call()
-    ms = kernel_ms(call, reps)[1]
+    ms = steps_kernel_ms(call, reps)[1]
     unique = 2 * len(src) * w.block_size * w.num_kv_heads * w.head_dim * (2 if w.dtype == "bf16" else 4)
     del k_priv, v_priv
     return ms, unique
@@ -282,8 +288,8 @@ def decode_entry(name, reps):
     if dw.decode_error_word() != 0:
         raise RuntimeError(f"{name}: kernel error word {dw.decode_error_word():#x}")
     nbytes = metrics.decode_bytes(w)
-    _, attn, merge = kernel_ms(dw.decode, reps)
-    prerot = kernel_ms(dw.decode_prerotated, reps)[1]
+    _, attn, merge = steps_kernel_ms(dw.decode, reps)
+    prerot = steps_kernel_ms(dw.decode_prerotated, reps)[1]
     gbs = nbytes / (attn * 1e-3) / 1e9
     e = {"workload": f"decode step after {name.replace('d', 'c', 1)}: one query row per request (its last "
                      f"context token)", "requests": int(w.num_reqs), "context_tokens": int(w.ctx_len.sum()),
@@ -316,8 +322,16 @@ def suite_entry(name, reps):
     pairs = metrics.workload_pairs(w)
     flops = metrics.attention_flops(pairs, w.num_q_heads, w.head_dim)
     nbytes = algorithmic_bytes(w)
-    plan, attn, merge = kernel_ms(dw.attend, reps)
-    prerot = kernel_ms(dw.attend_prerotated, reps)[1]
+    # the step sequence of the main measurement: write_kv, then the call
+    def step():
+        dw.write_new()
+        dw.attend()
+
+    def step_prerotated():
+        dw.write_new()
+        dw.attend_prerotated()
+    plan, attn, merge = steps_kernel_ms(step, reps)
+    prerot = steps_kernel_ms(step_prerotated, reps)[1]
     tf = flops / (attn * 1e-3) / 1e12
     e = {"workload": WORKLOADS[name], "query_tokens": int(w.total_q), "gflop": round(flops / 1e9, 3),
          "algorithmic_MB": round(nbytes / 1e6, 1),
@@ -357,8 +371,8 @@ def sweeps(reps=10):
             dw.attend()
             dw.attend_prerotated()
         torch.cuda.synchronize()
-        plan, attn, merge = kernel_ms(dw.attend, reps)
-        prerot = kernel_ms(dw.attend_prerotated, reps)[1]
+        plan, attn, merge = steps_kernel_ms(dw.attend, reps)
+        prerot = steps_kernel_ms(dw.attend_prerotated, reps)[1]
         flops = metrics.attention_flops(metrics.workload_pairs(w), w.num_q_heads, w.head_dim)
         rec = {"sweep": sweep, "x": x, "context_tokens": int(L), "query_tokens": int(w.total_q),
                "call_ms": round(plan + attn + merge, 5), "attention_kernel_ms": round(attn, 5),
@@ -445,19 +459,20 @@ def main():
     wall = time.perf_counter() - t0
     log(f"[bench] {ms_step:.4f} ms/step (wall {wall:.3f} s)")
 
-    # ---- per-call durations on the launch stream (HIP events)
+    # ---- the same timed steps again, with the HIP events the library records
+    # around each of its launches on the launch stream (no wait between
+    # steps): the kernels' durations inside the step sequence
+    ms_plan, ms_kernel, ms_merge = steps_kernel_ms(dw.step, a.steps)
+    ms_attn = ms_plan + ms_kernel + ms_merge
+    # the pre-rotated reference kernel in the same sequence (write_kv, then the call)
+    def step_prerotated():
+        dw.write_new()
+        dw.attend_prerotated()
+    _, ms_kernel_prerot, _ = steps_kernel_ms(step_prerotated, a.steps)
     reps = max(a.steps, 20)
-    ms_attn = timed(dw.attend, reps)
-    ms_prerot = timed(dw.attend_prerotated, reps)
     ms_wkv = timed(dw.write_new, reps)
-    log(f"[bench] attn {ms_attn:.4f} ms, prerotated {ms_prerot:.4f} ms, write_kv {ms_wkv:.4f} ms")
-
-    # ---- the attention kernel alone: HIP events recorded by the library
-    # around each launch, on the launch stream
-    ms_plan, ms_kernel, ms_merge = kernel_ms(dw.attend, reps)
-    ms_kernel_prerot = kernel_ms(dw.attend_prerotated, reps)[1]
-    log(f"[bench] kernels: plan {ms_plan:.4f} ms, attention {ms_kernel:.4f} ms, merge {ms_merge:.4f} ms, "
-        f"attention without RoPE {ms_kernel_prerot:.4f} ms")
+    log(f"[bench] kernels in the timed steps: plan {ms_plan:.4f} ms, attention {ms_kernel:.4f} ms, "
+        f"merge {ms_merge:.4f} ms; attention without RoPE {ms_kernel_prerot:.4f} ms; write_kv {ms_wkv:.4f} ms")
 
     tflops = flops / (ms_kernel * 1e-3) / 1e12
     call_tflops = flops / (ms_attn * 1e-3) / 1e12
@@ -515,11 +530,10 @@ def main():
         "tflops_attention_kernel": round(tflops, 2),
         "pct_mfma_bf16_peak_attention_kernel": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "kernels": {
-            "prefill_attn_ms": round(ms_attn, 5),
+            "prefill_attn_kernels_ms": round(ms_attn, 5),
             "plan_kernels_ms": round(ms_plan, 5),
             "attention_kernel_ms": round(ms_kernel, 5),
             "merge_kernel_ms": round(ms_merge, 5),
-            "reference_prerotated_ms": round(ms_prerot, 5),
             "prerotated_attention_kernel_ms": round(ms_kernel_prerot, 5),
             "rope_overhead_pct": round(100 * (ms_kernel / ms_kernel_prerot - 1), 2),
             "pct_hbm_peak_attention_kernel": round(100 * algorithmic_bytes(w) / (ms_kernel * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),

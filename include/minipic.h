@@ -229,15 +229,23 @@ int minipic_decode_prerotated(const void* q, const void* k_cache, const void* v_
  * the calling host thread also records four HIP events on its stream, around
  * the planning kernels (none for decode), the attention kernel and the merge
  * kernel.
+ * Switching timing on (or off) forgets the calls timed before.
  * minipic_kernel_times waits for the most recent such call of the thread to
  * finish and writes the three durations in milliseconds to ms[0..2] (plan,
- * attention, merge). It returns MINIPIC_ERR_INVALID_ARG when timing is off
- * or no call was timed yet, MINIPIC_ERR_HIP when the events fail. The events
- * belong to the library (one set per host thread, kept until the process
- * ends); calls on several streams from one thread overwrite each other's.
+ * attention, merge).
+ * minipic_kernel_times_all waits for the most recent call and writes the
+ * three durations of every call timed since timing was switched on, oldest
+ * first, to ms[3 c .. 3 c + 2] for call c < *num_calls; *num_calls is at most
+ * max_calls and at most 4096 (only the latest 4096 calls are kept). It lets a
+ * caller time a run of calls without waiting after each one.
+ * Both return MINIPIC_ERR_INVALID_ARG when timing is off, no call was timed
+ * yet or a pointer is NULL, MINIPIC_ERR_HIP when the events fail. The events
+ * belong to the library (one set of four per kept call and host thread, kept
+ * until the process ends).
  */
 int minipic_set_kernel_timing(int enable);
 int minipic_kernel_times(float* ms);
+int minipic_kernel_times_all(float* ms, int32_t max_calls, int32_t* num_calls);
 
 #ifdef __cplusplus
 }

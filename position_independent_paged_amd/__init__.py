@@ -10,7 +10,8 @@ from ._binding import (BlockCache, MINIPIC_ERR_CACHE_FULL, MINIPIC_ERR_CONTRACT,
                        MINIPIC_EW_CTX, MINIPIC_EW_POS, MINIPIC_EW_QCTX, MINIPIC_F32, MINIPIC_FLAG_ROTATE_Q,
                        LIB_PATH, MinipicError, load_library, minipic_batch, minipic_get_launch_info,
                        minipic_decode_attn, minipic_decode_prerotated, minipic_decode_workspace_size,
-                       minipic_kernel_times, minipic_prefill_attn, minipic_reference_prerotated,
+                       minipic_kernel_times, minipic_kernel_times_all, minipic_prefill_attn,
+                       minipic_reference_prerotated,
                        minipic_rope_table, minipic_set_kernel_timing, minipic_version, minipic_workspace_size,
                        minipic_write_kv)
 
@@ -19,7 +20,7 @@ __all__ = [
     "BlockCache", "MINIPIC_ERR_CACHE_FULL", "MINIPIC_ERR_CONTRACT", "minipic_describe_blocks", "minipic_slot_mapping",
     "EXPORTS", "LIB_PATH", "MinipicError", "load_library", "minipic_batch", "minipic_get_launch_info",
     "minipic_prefill_attn", "minipic_reference_prerotated", "minipic_rope_table", "minipic_version",
-    "minipic_set_kernel_timing", "minipic_kernel_times", "minipic_decode_workspace_size",
+    "minipic_set_kernel_timing", "minipic_kernel_times", "minipic_kernel_times_all", "minipic_decode_workspace_size",
     "minipic_decode_attn", "minipic_decode_prerotated",
     "minipic_workspace_size", "minipic_write_kv", "MINIPIC_BF16", "MINIPIC_F32", "MINIPIC_BLK_PDEP",
     "MINIPIC_BLK_GLOBAL", "MINIPIC_FLAG_ROTATE_Q", "MINIPIC_EW_BLOCK", "MINIPIC_EW_POS", "MINIPIC_EW_QCTX",

@@ -29,6 +29,7 @@ EXPORTS = [
     "minipic_version", "minipic_status_string", "minipic_last_error", "minipic_rope_table",
     "minipic_write_kv", "minipic_workspace_size", "minipic_get_launch_info", "minipic_prefill_attn",
     "minipic_reference_prerotated", "minipic_set_kernel_timing", "minipic_kernel_times",
+    "minipic_kernel_times_all",
     "minipic_decode_workspace_size", "minipic_decode_attn", "minipic_decode_prerotated",
     "minipic_describe_blocks", "minipic_block_cache_create", "minipic_block_cache_destroy",
     "minipic_block_cache_assign", "minipic_slot_mapping",
@@ -109,6 +110,8 @@ def load_library(path: str = LIB_PATH):
     lib.minipic_slot_mapping.argtypes = [vp, vp, i64, i32, vp, vp, ctypes.POINTER(i64)]
     lib.minipic_set_kernel_timing.argtypes = [ctypes.c_int]
     lib.minipic_kernel_times.argtypes = [ctypes.POINTER(ctypes.c_float)]
+    lib.minipic_kernel_times_all.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_int32,
+                                             ctypes.POINTER(ctypes.c_int32)]
     for name in EXPORTS[3:]:
         if name not in ("minipic_block_cache_create", "minipic_block_cache_destroy"):
             getattr(lib, name).restype = ctypes.c_int
@@ -198,6 +201,14 @@ def minipic_kernel_times() -> tuple:
     ms = (ctypes.c_float * 3)()
     _check(load_library().minipic_kernel_times(ms))
     return float(ms[0]), float(ms[1]), float(ms[2])
+
+
+def minipic_kernel_times_all(max_calls: int = 4096) -> list:
+    """(plan, attention, merge) milliseconds of every attention call timed since timing was switched on."""
+    ms = (ctypes.c_float * (3 * max_calls))()
+    n = ctypes.c_int32(0)
+    _check(load_library().minipic_kernel_times_all(ms, max_calls, ctypes.byref(n)))
+    return [(float(ms[3 * c]), float(ms[3 * c + 1]), float(ms[3 * c + 2])) for c in range(n.value)]
 
 
 def minipic_decode_workspace_size(batch: minipic_batch, dtype_code: int) -> int:

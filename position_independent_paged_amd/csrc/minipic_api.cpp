@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <vector>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -94,21 +95,29 @@ int check_batch(const minipic_batch* b, int dtype) {
 }
 
 // Optional kernel timing (minipic_set_kernel_timing): events recorded on the
-// call's stream around the three launches of the latest call of this thread.
+// call's stream around the three launches of each call of this thread, one
+// set of four per call for up to kTimedCalls calls since timing was switched
+// on (later calls reuse the sets in turn). Events are created on first use
+// and kept until the process ends.
+constexpr int kTimedCalls = 4096;
 struct KernelTimer {
   bool on = false;
-  bool valid = false;
-  hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
+  bool valid = false;      // the latest call was timed completely
+  int64_t calls = 0;       // calls begun since timing was switched on
+  std::vector<hipEvent_t> ev;   // [kTimedCalls][4]
 };
 thread_local KernelTimer g_timer;
 
 hipError_t timer_mark(int i, hipStream_t s) {
   if (!g_timer.on) return hipSuccess;
-  if (!g_timer.ev[i]) {
-    hipError_t e = hipEventCreate(&g_timer.ev[i]);
-    if (e != hipSuccess) return e;
+  if (i == 0) ++g_timer.calls;
+  if (g_timer.ev.empty()) g_timer.ev.assign((size_t)kTimedCalls * 4, nullptr);
+  hipEvent_t& e = g_timer.ev[(size_t)((g_timer.calls - 1) % kTimedCalls) * 4 + i];
+  if (!e) {
+    hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) return r;
   }
-  return hipEventRecord(g_timer.ev[i], s);
+  return hipEventRecord(e, s);
 }
 
 // Decode plan (host scalars only): key splits per (request, KV head) so that
@@ -513,15 +522,34 @@ int minipic_decode_prerotated(const void* q, const void* k_cache, const void* v_
 int minipic_set_kernel_timing(int enable) {
   g_timer.on = enable != 0;
   g_timer.valid = false;
+  g_timer.calls = 0;
   return MINIPIC_OK;
 }
 
 int minipic_kernel_times(float* ms) {
   if (!ms) return fail(MINIPIC_ERR_INVALID_ARG, "ms is NULL");
   if (!g_timer.on || !g_timer.valid) return fail(MINIPIC_ERR_INVALID_ARG, "no timed call (timing is off or no call yet)");
-  hipError_t e = hipEventSynchronize(g_timer.ev[3]);
-  for (int i = 0; i < 3 && e == hipSuccess; ++i) e = hipEventElapsedTime(&ms[i], g_timer.ev[i], g_timer.ev[i + 1]);
+  const hipEvent_t* ev = &g_timer.ev[(size_t)((g_timer.calls - 1) % kTimedCalls) * 4];
+  hipError_t e = hipEventSynchronize(ev[3]);
+  for (int i = 0; i < 3 && e == hipSuccess; ++i) e = hipEventElapsedTime(&ms[i], ev[i], ev[i + 1]);
   if (e != hipSuccess) return hip_fail(e, "kernel timing events");
+  return MINIPIC_OK;
+}
+
+int minipic_kernel_times_all(float* ms, int32_t max_calls, int32_t* num_calls) {
+  if (!ms || !num_calls || max_calls < 0) return fail(MINIPIC_ERR_INVALID_ARG, "ms / num_calls NULL or max_calls < 0");
+  if (!g_timer.on || !g_timer.valid) return fail(MINIPIC_ERR_INVALID_ARG, "no timed call (timing is off or no call yet)");
+  const int64_t kept = g_timer.calls < kTimedCalls ? g_timer.calls : kTimedCalls;
+  const int64_t n = kept < max_calls ? kept : max_calls;
+  const hipEvent_t* last = &g_timer.ev[(size_t)((g_timer.calls - 1) % kTimedCalls) * 4];
+  hipError_t e = hipEventSynchronize(last[3]);
+  for (int64_t c = 0; c < n && e == hipSuccess; ++c) {
+    const int64_t call = g_timer.calls - kept + c;   // oldest kept call first
+    const hipEvent_t* ev = &g_timer.ev[(size_t)(call % kTimedCalls) * 4];
+    for (int i = 0; i < 3 && e == hipSuccess; ++i) e = hipEventElapsedTime(&ms[3 * c + i], ev[i], ev[i + 1]);
+  }
+  if (e != hipSuccess) return hip_fail(e, "kernel timing events");
+  *num_calls = (int32_t)n;
   return MINIPIC_OK;
 }
 

@@ -297,3 +297,28 @@ def test_deterministic():
     dw.attend()
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), dw.out.view(torch.int16))
+
+
+def test_kernel_timing_of_a_run_of_calls():
+    """The timing record keeps every call made while timing is on and does not change the result."""
+    from position_independent_paged_amd import (minipic_kernel_times, minipic_kernel_times_all,
+                                                minipic_set_kernel_timing)
+    w = workload.make_config("c3_small")
+    say("kernel timing c3_small")
+    dw = stage(w)
+    dw.step()
+    torch.cuda.synchronize()
+    ref = dw.out.clone()
+    minipic_set_kernel_timing(True)
+    try:
+        for _ in range(5):
+            dw.attend()
+        times = minipic_kernel_times_all(16)
+        last = minipic_kernel_times()
+    finally:
+        minipic_set_kernel_timing(False)
+    assert len(times) == 5
+    for t in times:
+        assert all(x > 0 for x in t), t
+    assert last == times[-1]
+    assert torch.equal(ref.view(torch.int16), dw.out.view(torch.int16))

@@ -217,3 +217,18 @@ def test_bf16_rounding_is_rne():
     back = workload.bf16_bits_to_f32(b)
     assert back[0] == 1.0 and back[1] == 1.0 and back[2] == 1.015625 and back[3] == -2.5
     assert np.isinf(back[5])
+
+
+def test_kernel_timing_rejects_reads_without_timed_calls():
+    lib = pip.load_library()
+    ms = (ctypes.c_float * 6)()
+    n = ctypes.c_int32(-1)
+    assert lib.minipic_set_kernel_timing(0) == 0
+    assert lib.minipic_kernel_times(ms) == pip.MinipicError(-1, "").status
+    assert lib.minipic_kernel_times_all(ms, 2, ctypes.byref(n)) == -1
+    assert lib.minipic_set_kernel_timing(1) == 0
+    assert lib.minipic_kernel_times_all(ms, 2, ctypes.byref(n)) == -1   # timing on, nothing timed yet
+    assert lib.minipic_kernel_times_all(None, 2, ctypes.byref(n)) == -1
+    assert lib.minipic_kernel_times_all(ms, -1, ctypes.byref(n)) == -1
+    assert n.value == -1
+    assert lib.minipic_set_kernel_timing(0) == 0
