@@ -367,7 +367,7 @@ def sweeps(reps=10):
         w = workload.custom(f"{sweep}{x}", [segs], max_pos=max(32768, L), seed=x, **shape)
         dw = DeviceWorkload(w, device="cuda:0")
         dw.write_new()
-        for _ in range(2):
+        for _ in range(20):   # warm-up: the GPU settles under a few tens of ms of load
             dw.attend()
             dw.attend_prerotated()
         torch.cuda.synchronize()
