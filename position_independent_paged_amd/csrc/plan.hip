@@ -22,22 +22,19 @@ namespace minipic {
 // positions, `L` its context length. pos0 is set when the block's positions
 // (those of its tokens below L) run pos0, pos0+1, ... and the whole run
 // pos0 .. pos0+15 lies inside the cos/sin table.
-__device__ __forceinline__ BlkDesc make_blk(const PlanParams& P, const int32_t* btab, const int32_t* lpos, int L,
-                                            int kb, int span, int flags, int full) {
-  int ph = btab[kb];
+__device__ __forceinline__ BlkDesc blk_from(const PlanParams& P, int ph, const int4 (&pp)[kBlock / 4], int L, int kb,
+                                            int span, int flags, int full) {
   if (ph < 0 || (int64_t)ph >= P.num_blocks) {
     atomicOr(&P.hdr->err, (uint32_t)MINIPIC_EW_BLOCK);
     ph = -1;  // read as zeros by the attention kernels
   }
-  const int4* pp = (const int4*)(lpos + (int64_t)kb * kBlock);
   int p[kBlock];
 #pragma unroll
   for (int i = 0; i < kBlock / 4; ++i) {
-    const int4 v = pp[i];
-    p[4 * i] = v.x;
-    p[4 * i + 1] = v.y;
-    p[4 * i + 2] = v.z;
-    p[4 * i + 3] = v.w;
+    p[4 * i] = pp[i].x;
+    p[4 * i + 1] = pp[i].y;
+    p[4 * i + 2] = pp[i].z;
+    p[4 * i + 3] = pp[i].w;
   }
   const int nvalid = min(kBlock, L - kb * kBlock);
   bool cons = p[0] >= 0 && p[0] <= P.max_pos - kBlock;
@@ -46,13 +43,26 @@ __device__ __forceinline__ BlkDesc make_blk(const PlanParams& P, const int32_t* 
   return BlkDesc{kb, ph, span, flags, cons ? p[0] : -1, full, 0, 0};
 }
 
+__device__ __forceinline__ BlkDesc make_blk(const PlanParams& P, int ph, const int32_t* lpos, int L, int kb, int span,
+                                            int flags, int full) {
+  const int4* src = (const int4*)(lpos + (int64_t)kb * kBlock);
+  int4 pp[kBlock / 4];
+#pragma unroll
+  for (int i = 0; i < kBlock / 4; ++i) pp[i] = src[i];
+  return blk_from(P, ph, pp, L, kb, span, flags, full);
+}
+
 template <int BQ, int NT>
 __global__ void __launch_bounds__(NT) plan_tiles_kernel(PlanParams P) {
   static_assert(BQ <= NT, "one query token per thread");
+  constexpr int BPT = kPlanBlocksPerThread;
+  constexpr int PASS = NT * BPT;   // key blocks per pass, each thread owning BPT consecutive ones
   __shared__ int qblk[BQ];
   __shared__ int e_bq[BQ], e_span[BQ], e_pdep[BQ];
   __shared__ int tmp[NT / 64];
   __shared__ int s_hi, s_lo, s_anyp, s_phi;
+  __shared__ int s_span[PASS];     // span ids and flags of the first pass's blocks
+  __shared__ uint8_t s_flg[PASS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -60,6 +70,25 @@ __global__ void __launch_bounds__(NT) plan_tiles_kernel(PlanParams P) {
   const int r = t / P.nqt;
   const int qt = t % P.nqt;
   TileDesc* td = P.tiles + t;
+  const int32_t* span = P.span_id + (int64_t)r * P.max_blocks;
+  const uint8_t* flg = P.blk_flags + (int64_t)r * P.max_blocks;
+  const int32_t* btab = P.block_table + (int64_t)r * P.max_blocks;
+  const int32_t* lpos = P.logical_pos + (int64_t)r * P.max_blocks * kBlock;
+
+  // The span ids, flags and physical blocks of the first pass's blocks depend
+  // only on the request: they are loaded before anything else, together with
+  // the request's offsets, so the tile's dependent round trips are the
+  // offsets, the query contexts and the positions of its visible blocks.
+  const int nb0 = P.max_blocks < PASS ? P.max_blocks : PASS;
+  int f0[BPT], s0[BPT], ph0[BPT];
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    const int kb = tid * BPT + j;
+    const bool in = kb < nb0;
+    f0[j] = in ? flg[kb] : 0;
+    s0[j] = in ? span[kb] : 0;
+    ph0[j] = in ? btab[kb] : -1;
+  }
   const int qb = P.q_indptr[r];
   const int qe = P.q_indptr[r + 1];
   const int row0 = qb + qt * BQ;
@@ -74,16 +103,24 @@ __global__ void __launch_bounds__(NT) plan_tiles_kernel(PlanParams P) {
     if (tid == 0) atomicOr(&P.hdr->err, (uint32_t)MINIPIC_EW_CTX);
     L = L < 0 ? 0 : Lmax;
   }
-  const int32_t* span = P.span_id + (int64_t)r * P.max_blocks;
-  const uint8_t* flg = P.blk_flags + (int64_t)r * P.max_blocks;
-  const int32_t* btab = P.block_table + (int64_t)r * P.max_blocks;
-  const int32_t* lpos = P.logical_pos + (int64_t)r * P.max_blocks * kBlock;
+  const int cq = tid < nq ? P.q_ctx_idx[row0 + tid] : 0;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    const int kb = tid * BPT + j;
+    if (kb < nb0) {
+      s_span[kb] = s0[j];
+      s_flg[kb] = (uint8_t)f0[j];
+    }
+  }
+  __syncthreads();
+  auto span_at = [&](int b) { return b < nb0 ? s_span[b] : span[b]; };
+  auto flg_at = [&](int b) { return b < nb0 ? (int)s_flg[b] : (int)flg[b]; };
 
   // ---- query tokens
   bool valid = tid < nq;
   int c = -1;
   if (valid) {
-    c = P.q_ctx_idx[row0 + tid];
+    c = cq;
     if (c < 0 || c >= L) {
       atomicOr(&P.hdr->err, (uint32_t)MINIPIC_EW_QCTX);
       c = c < 0 ? 0 : L - 1;
@@ -93,8 +130,8 @@ __global__ void __launch_bounds__(NT) plan_tiles_kernel(PlanParams P) {
   const int bq = valid ? (c >> 4) : -1;
   int sp = 0, pd = 0;
   if (valid) {
-    sp = span[bq];
-    pd = (flg[bq] & MINIPIC_BLK_PDEP) ? 1 : 0;
+    sp = span_at(bq);
+    pd = (flg_at(bq) & MINIPIC_BLK_PDEP) ? 1 : 0;
   }
   if (tid < BQ) {
     P.toks[(int64_t)t * BQ + tid] = TokDesc{valid ? c : -1, sp, pd, 0};
@@ -135,11 +172,11 @@ __global__ void __launch_bounds__(NT) plan_tiles_kernel(PlanParams P) {
     // start of the run of equal span ids that holds the smallest query block
     int lo = 0;
     if (!anyp && mn != INT_MAX) {
-      const int s0 = span[mn];
+      const int sm = span_at(mn);
       int base = mn;
       while (true) {
         const int b = base - 1 - lane;
-        const bool stop = (b < 0) || (span[b] != s0);
+        const bool stop = (b < 0) || (span_at(b) != sm);
         const uint64_t m = __ballot(stop);
         if (m) {
           lo = base - (__ffsll((unsigned long long)m) - 1);
@@ -160,13 +197,12 @@ __global__ void __launch_bounds__(NT) plan_tiles_kernel(PlanParams P) {
 
   // ---- compacted list, in block order: the GLOBAL blocks below lo (visible
   // to every row, below every query block) and the blocks of [lo, hi] some row
-  // sees. A pass covers NT * BPT blocks, each thread owning BPT consecutive
-  // ones, so all loads of a pass are in flight together and one scan places
-  // the visible blocks.
-  constexpr int BPT = kPlanBlocksPerThread;
+  // sees. A pass covers PASS blocks, each thread owning BPT consecutive ones,
+  // so all loads of a pass are in flight together (the first pass's were
+  // loaded at the start) and one scan places the visible blocks.
   BlkDesc* out = P.blist + (int64_t)t * P.max_blocks;
   int n = 0;
-  for (int base = 0; base <= hi; base += NT * BPT) {
+  for (int base = 0; base <= hi; base += PASS) {
     int f[BPT], s[BPT];
     bool vis[BPT], full[BPT];
     int cnt = 0;
@@ -178,8 +214,8 @@ __global__ void __launch_bounds__(NT) plan_tiles_kernel(PlanParams P) {
       vis[j] = false;
       full[j] = true;
       if (kb <= hi) {
-        f[j] = flg[kb];
-        s[j] = span[kb];
+        f[j] = base == 0 ? f0[j] : flg[kb];
+        s[j] = base == 0 ? s0[j] : span[kb];
         if (kb < lo) {
           vis[j] = (f[j] & MINIPIC_BLK_GLOBAL) != 0;
         } else {
@@ -197,7 +233,10 @@ __global__ void __launch_bounds__(NT) plan_tiles_kernel(PlanParams P) {
     int off = block_excl_scan<NT>(cnt, tmp, &tot);
 #pragma unroll
     for (int j = 0; j < BPT; ++j)
-      if (vis[j]) out[n + off++] = make_blk(P, btab, lpos, L, base + tid * BPT + j, s[j], f[j], full[j] ? 1 : 0);
+      if (vis[j]) {
+        const int kb = base + tid * BPT + j;
+        out[n + off++] = make_blk(P, base == 0 ? ph0[j] : btab[kb], lpos, L, kb, s[j], f[j], full[j] ? 1 : 0);
+      }
     n += tot;
   }
   if (tid == 0) *td = TileDesc{r, row0, nq, n, 0, -1, 0, 0};
@@ -252,13 +291,26 @@ __global__ void __launch_bounds__(kItemThreads) plan_items_kernel(PlanParams P) 
   __shared__ unsigned long long red[NT / 64];
   __shared__ int tmp[NT / 64];
   __shared__ int bins[kQueues * kCostBins];
+  // fields of the first kTileCache tiles, read or computed once: list length,
+  // first item, request, first query row, first partial slot, query tokens |
+  // pieces << 16
   __shared__ int s_nl[kTileCache];
   __shared__ int s_ioff[kTileCache];
+  __shared__ int s_r[kTileCache];
+  __shared__ int s_row0[kTileCache];
+  __shared__ int s_slot0[kTileCache];
+  __shared__ int s_nqns[kTileCache];
   const int tid = threadIdx.x;
   const int T = P.num_tiles;
   const int H = P.hkv;
   // list lengths of the tiles, read once (cached in LDS for up to kTileCache tiles)
-  for (int t = tid; t < T && t < kTileCache; t += NT) s_nl[t] = P.tiles[t].nlist;
+  for (int t = tid; t < T && t < kTileCache; t += NT) {
+    const TileDesc d = P.tiles[t];
+    s_nl[t] = d.nlist;
+    s_r[t] = d.r;
+    s_row0[t] = d.row0;
+    s_nqns[t] = d.nq;
+  }
   __syncthreads();
   auto nlist = [&](int t) { return t < kTileCache ? s_nl[t] : P.tiles[t].nlist; };
 
@@ -297,7 +349,11 @@ __global__ void __launch_bounds__(kItemThreads) plan_items_kernel(PlanParams P) 
       P.tiles[t].nsplit = ns;
       P.tiles[t].slot0 = ns > 1 ? slot_base + off : -1;
       P.tiles[t].item0 = item_base + ioff;
-      if (t < kTileCache) s_ioff[t] = item_base + ioff;
+      if (t < kTileCache) {
+        s_ioff[t] = item_base + ioff;
+        s_slot0[t] = ns > 1 ? slot_base + off : -1;
+        s_nqns[t] |= ns << 16;
+      }
     }
     slot_base += tot;
     item_base += itot;
@@ -379,7 +435,14 @@ __global__ void __launch_bounds__(kItemThreads) plan_items_kernel(PlanParams P) 
   TileDesc td{};
   for_my_pieces([&](int t, int s, int ns, int p0, int p1) {
     if (t != t_td) {
-      td = P.tiles[t];
+      if (t < kTileCache) {
+        td.r = s_r[t];
+        td.row0 = s_row0[t];
+        td.nq = s_nqns[t] & 0xffff;
+        td.slot0 = s_slot0[t];
+      } else {
+        td = P.tiles[t];
+      }
       t_td = t;
     }
     const int cost_bin = bin_index(0, p1 - p0);
@@ -393,11 +456,11 @@ __global__ void __launch_bounds__(kItemThreads) plan_items_kernel(PlanParams P) 
   int group_base = 0;
   for (int t0 = 0; t0 < T; t0 += NT) {
     const int t = t0 + tid;
-    const int ns = t < T ? P.tiles[t].nsplit : 0;
+    const int ns = t < T ? (t < kTileCache ? s_nqns[t] >> 16 : P.tiles[t].nsplit) : 0;
     int tot;
     const int off = block_excl_scan<NT>(ns > 1 ? H : 0, tmp, &tot);
     if (ns > 1) {
-      const int slot0 = P.tiles[t].slot0;
+      const int slot0 = t < kTileCache ? s_slot0[t] : P.tiles[t].slot0;
       for (int g = 0; g < H; ++g) P.groups[group_base + off + g] = Group{t, g, ns, slot0 + g * ns};
     }
     group_base += tot;
