@@ -322,3 +322,23 @@ def test_kernel_timing_of_a_run_of_calls():
         assert all(x > 0 for x in t), t
     assert last == times[-1]
     assert torch.equal(ref.view(torch.int16), dw.out.view(torch.int16))
+
+
+def test_parity_context_beyond_one_planning_pass():
+    """More than 2048 key blocks in one request: the planner's span-start search and its later passes
+    read block descriptors past the first pass (loaded at kernel start); the PDep rows' lists run over
+    nine staging passes of the attention kernel. Sampled span and PDep rows against the oracle."""
+    segs = [Segment("global", 64, fresh=False, pool=0)]
+    segs += [Segment("span", 240, fresh=False) for _ in range(140)]
+    segs += [Segment("span", 256), Segment("span", 256), Segment("pdep", 64)]
+    w = workload.custom("long", [segs], pool_lengths=[64], num_q_heads=8, num_kv_heads=2, head_dim=64,
+                        dtype="bf16", rope_theta=5e5, max_pos=65536, seed=11)
+    assert w.block_table.shape[1] > 2048
+    say(f"parity long context: ctx={w.max_ctx_len} blocks={w.block_table.shape[1]} total_q={w.total_q}")
+    dw = stage(w)
+    say(f"  plan {dw.launch_info()}")
+    dw.step()
+    torch.cuda.synchronize()
+    assert dw.error_word() == 0
+    got, want = compare_workload(w, out_f64(dw.out), rows_per_req=160, seed=2)
+    check("long", got, want, w.dtype)
