@@ -10,9 +10,9 @@
 // head, piece of the tile's visible-block list) from the per-XCD queues.
 //
 // One work item = 256 query rows = BQ query tokens x G query heads sharing
-// KV head g (G = Hq/Hkv). A work-group has 8/RB waves; wave w owns RB blocks
-// of 32 rows (rows 32 RB w + 32 rb + (l % 32)); every K or V fragment read
-// from LDS feeds RB MFMAs.
+// KV head g (G = Hq/Hkv). A work-group has NW waves (a build parameter, 8 by
+// default); wave w owns RB blocks of 32 rows (rows 32 RB w + 32 rb + (l % 32));
+// every K or V fragment read from LDS feeds RB MFMAs.
 //   * a pipeline step covers 32 keys = 2 cache blocks of the list.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: keys on the M side, queries on
 //     the N side, so lane l holds 16 keys of ONE query and the row max / sum
@@ -22,26 +22,32 @@
 //     consecutive elements then are the bf16x8 B operand of O^T += V^T P^T.
 //   * V is cached transposed inside each block ([d][16]): the V^T A operand
 //     is one 16-byte LDS read of 8 consecutive keys.
-//   * Software pipeline, per step s (one barrier per step):
-//       block 1: S(s+1) = K(s+1) Q^T on MFMA  |  P(s) = exp2(S(s) - m) on VALU
-//       block 2: O += V(s) P(s) on MFMA       |  rotate K(s+2) into LDS, store
-//                                                V(s+1), row max of S(s+1)
-//     then the loads of K(s+3), cos/sin(s+3), V(s+2) are issued and the
-//     running max is raised if S(s+1) needs it. The rotation (rotate-half,
-//     i <-> i + d/2) happens once per work item and tile, between the global
-//     load and the LDS store, in fp32 with one rounding to bf16.
+//   * q is scaled by scale * log2(e) when it is loaded and the QK MFMA chain
+//     starts from minus the running max, so the scores leave the MFMA in log2
+//     units already shifted: P = exp2(S) needs no multiply-add per score.
+//   * Software pipeline with one barrier per step: step s computes
+//     S(s+1) = K(s+1) Q^T and O += V(s) P(s) on MFMA, the softmax of the next
+//     scores, rotates and stores K(s+2) and stores V(s+1) (loaded two steps
+//     before), and issues the loads of K(s+4), cos/sin(s+4) and V(s+3). The
+//     two waves that share a SIMD take these parts in opposite order, so one
+//     issues MFMAs while the other runs vector work. The rotation
+//     (rotate-half, i <-> i + d/2) happens once per work item and tile,
+//     between the global load and the LDS store, in fp32 with one rounding to
+//     bf16.
 //   * Global loads are buffer loads: a wave's keys always lie in one cache
 //     block, so the block's base address is a scalar and an invalid block
 //     becomes a zero-size buffer whose loads return zeros.
 //   * The element-wise mask runs only on steps where some row does not see
 //     every key (plan_tiles marks fully visible blocks); it is a uniform branch.
-//   * Online softmax in log2 units with a lazily raised running max: the
-//     accumulators are rescaled only when a row max grows by more than 2^8,
-//     which is exact (numerator and denominator share the stale max). The
-//     row sums come from the PV MFMA itself (a constant all-ones A row), so
-//     they sum the same bf16 P as the numerator and cost no VALU adds.
-//   * A piece of a split tile stores fp32 (O, m, l) to its slot; the merge
-//     kernel combines the pieces.
+//   * Online softmax with a lazily raised running max: the accumulators are
+//     rescaled only when a score exceeds the running max by more than 8 (in
+//     log2 units), which is exact (numerator and denominator share the stale
+//     max). The row sums add the same bf16 P the numerator uses, two at a time
+//     with v_dot2_f32_bf16.
+//   * q rows come in and the output goes out through an LDS row buffer, so
+//     every global load or store instruction moves whole rows.
+//   * A piece of a split tile stores fp32 (O, m, l) to its slot (O in the
+//     lanes' order); the merge kernel combines the pieces.
 #include "common.h"
 
 namespace minipic {
