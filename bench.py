@@ -59,6 +59,8 @@ WORKLOADS = {
           "Hq 32, Hkv 8, d 128, bf16, RoPE base 5e5",
     "c3": "8B shape: 16 requests, each 10 of 40 shared cached 192-token spans in random order + 64-token PDep "
           "question; Hq 32, Hkv 8, d 128, bf16, RoPE base 5e5",
+    "c3w": "8B shape, retrieval batch: 64 requests, each 10 of 160 shared cached documents of 100 tokens padded "
+           "to 112, in random order, + 64-token PDep question; Hq 32, Hkv 8, d 128, bf16, RoPE base 5e5",
     "c4": "8B shape long context: 1 request, 120 SSep spans of 256 (60 cached, 60 fresh) + 512-token PDep suffix; "
           "Hq 32, Hkv 8, d 128, bf16, RoPE base 5e5",
     "c5": "70B shape: 8 requests, shared cached 256-token GLOBAL prefix + 20 fresh SSep spans of U{128..512} "
@@ -78,7 +80,7 @@ def parse():
     ap.add_argument("--config", default="c4", choices=sorted(k for k in WORKLOADS if k.startswith("c")))
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample (0 disables the cpu_baseline leg)")
-    ap.add_argument("--suite", default="c2,c3,c5,e2,e4,d2,d3,d4,d5",
+    ap.add_argument("--suite", default="c2,c3,c3w,c5,e2,e4,d2,d3,d4,d5",
                     help="other workloads whose attention is timed beside the main one (empty: none)")
     ap.add_argument("--sweeps", action="store_true",
                     help="only run the kernel sweeps that mirror the pages' preload / TTFT figure and print "
@@ -339,7 +341,7 @@ def suite_entry(name, reps):
          "tflops_kernel": round(tf, 2), "pct_mfma_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
          "pct_hbm_peak": round(100 * nbytes / (attn * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
          "prerotated_kernel_ms": round(prerot, 5), "rope_overhead_pct": round(100 * (attn / prerot - 1), 2)}
-    if name == "c3":
+    if name in ("c3", "c3w"):   # shared documents at different offsets
         ms, unique = private_copy_prerotated(dw, w, reps)
         e["prerotated_private_copies_kernel_ms"] = round(ms, 5)
         e["prerotated_private_copies_unique_kv_MB"] = round(unique / 1e6, 1)

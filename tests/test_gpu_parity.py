@@ -139,7 +139,7 @@ def test_write_kv_scattered_and_skipped_slots():
 # attention parity
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["c1", "c1_cached", "c3_small", "c4_small", "c5_small", "c2", "c3", "e2",
+@pytest.mark.parametrize("name", ["c1", "c1_cached", "c3_small", "c4_small", "c5_small", "c2", "c3", "c3w", "e2",
                                   "e4_small"])
 def test_parity_all_rows(name):
     w = workload.make_config(name)

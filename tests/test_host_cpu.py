@@ -190,6 +190,10 @@ def test_pair_counts_of_benchmark_layouts():
     w4 = workload.make_config("c4")
     want4 = 60 * tri(256) + sum(30720 + i + 1 for i in range(512))
     assert metrics.workload_pairs(w4) == want4
+    # c3w: 64 requests, a 64-token PDep question over 10 documents of 112 tokens each
+    w3w = workload.make_config("c3w")
+    assert w3w.num_reqs == 64 and int(w3w.ctx_len.max()) == 10 * 112 + 64
+    assert metrics.workload_pairs(w3w) == 64 * sum(1120 + i + 1 for i in range(64))
 
 
 def test_generator_layout_invariants():

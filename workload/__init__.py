@@ -332,6 +332,14 @@ def _c3(seed=3, num_reqs=16, pool=40, span_len=192, per_req=10, q_len=64, name="
                  head_dim=128, dtype="bf16", rope_theta=5e5, max_pos=32768, seed=seed, rng=rng)
 
 
+def _c3w(seed=3, name="c3w"):
+    """The retrieval stand-in at the batch size of the pages' throughput table:
+    64 requests, each 10 of 160 cached documents of 100 tokens (padded to 112)
+    in random order plus a 64-token PDep question (the pool keeps c3's four
+    uses per document)."""
+    return _c3(seed, num_reqs=64, pool=160, span_len=pad_to_block(100), per_req=10, q_len=64, name=name)
+
+
 def _c4(seed=4, n_spans=120, span_len=256, suffix=512, name="c4"):
     """Long context: 120 SSep spans of 256 tokens, a seeded half of them cached and
     the other half computed now, then a 512-token PDep suffix."""
@@ -402,6 +410,7 @@ CONFIGS = {
     "c1": _c1,
     "c2": _c2,
     "c3": _c3,
+    "c3w": _c3w,
     "c4": _c4,
     "c5": _c5,
 }
