@@ -205,7 +205,20 @@ def cpu_baseline(w, target_s, seed=0):
         n, t = run(n)
     return {"value": n / t, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{n} query rows drawn uniformly from the {int(counts.sum())} of workload {w.name}, "
-                      f"float64 numpy oracle, {t:.1f} s"}
+                      f"float64 numpy oracle, {t:.1f} s",
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
+
+
+def cpu_model():
+    """Model name of the host CPU (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def algorithmic_bytes(w):
@@ -222,6 +235,38 @@ def algorithmic_bytes(w):
     kv = 2 * len(blocks) * w.block_size * w.num_kv_heads * w.head_dim * elem
     cs = len(positions) * w.head_dim * 4
     return qo + kv + cs
+
+
+def graph_steps(step, ms_step, reps=5):
+    """ms per step of `step` replayed from one captured HIP graph of N steps
+    (N so that one replay takes >= 50 ms), median over `reps` replays."""
+    import statistics
+    import torch
+    n = max(10, min(2000, int(50.0 / max(ms_step, 1e-3)) + 1))
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()                            # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for _ in range(n):
+            step()
+    g.replay()                            # first replay uploads the graph
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / n)
+    del g
+    return {"ms_per_step_median": round(statistics.median(times), 5), "reps": reps, "steps_per_replay": n,
+            "ms_per_step_all": [round(t, 5) for t in times]}
 
 
 def steps_kernel_ms(step, n):
@@ -461,6 +506,12 @@ def main():
     wall = time.perf_counter() - t0
     log(f"[bench] {ms_step:.4f} ms/step (wall {wall:.3f} s)")
 
+    # ---- the same steps replayed from a captured HIP graph (no launch gaps):
+    # one graph of enough steps for >= 50 ms, replayed 5 times, median
+    graph = graph_steps(dw.step, ms_step, reps=5)
+    log(f"[bench] graph replay: {graph['ms_per_step_median']:.4f} ms/step (median of {graph['reps']} replays of "
+        f"{graph['steps_per_replay']} steps)")
+
     # ---- the same timed steps again, with the HIP events the library records
     # around each of its launches on the launch stream (no wait between
     # steps): the kernels' durations inside the step sequence
@@ -478,8 +529,11 @@ def main():
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
 
     def step_cold():
+        # this step's K/V are written first, then the caches are flushed, so the
+        # attention kernel reads every K/V block, q row and table row from HBM
+        dw.write_new()
         scratch.fill_(1)
-        dw.step()
+        dw.attend()
     ms_plan_cold, ms_kernel_cold, ms_merge_cold = steps_kernel_ms(step_cold, a.steps)
     del scratch
     reps = max(a.steps, 20)
@@ -540,6 +594,7 @@ def main():
             "gflop_per_step": round(flops / 1e9, 3),
         },
         "tflops_step": round(step_tflops, 2),
+        "graph_replay": graph,
         "tflops_attention_call": round(call_tflops, 2),
         "tflops_attention_kernel": round(tflops, 2),
         "pct_mfma_bf16_peak_attention_kernel": round(100 * tflops / PEAK_BF16_TFLOPS, 2),

@@ -60,6 +60,8 @@ extern "C" {
 #define MINIPIC_EW_POS     2u  /* a logical position was outside [0, max_pos) */
 #define MINIPIC_EW_QCTX    4u  /* a q_ctx_idx entry was outside [0, ctx_len) */
 #define MINIPIC_EW_CTX     8u  /* ctx_len exceeded max_blocks_per_req * block_size */
+#define MINIPIC_EW_SPAN   16u  /* a query's span id also names a block before its own run
+                                  (the span-id contract of minipic_batch is broken) */
 
 /*
  * One batch of prefill requests. Host scalars plus device arrays.
@@ -75,15 +77,22 @@ extern "C" {
  * query at context index c and a key at context index j, with bc = c / 16 and
  * bj = j / 16:
  *     j <= c  and  ( PDEP(bc)  or  GLOBAL(bj)  or  span_id[bj] == span_id[bc] )
- * Contract: a span_id value names ONE contiguous run of blocks of a request
- * (runs are found by scanning neighbours; a value that reappears after another
- * value is a different, invisible span). Causality is by context index, not by
- * logical position. Pad tokens are ordinary tokens.
+ * Contract: a span_id value names ONE contiguous run of blocks of a request.
+ * The span test is evaluated on runs (found by scanning neighbours): a block
+ * that carries a query's span id but lies before the start of the query's own
+ * run is a different span and is not attended; when such a block exists (the
+ * contract is broken) the attention calls also set MINIPIC_EW_SPAN in the
+ * workspace error word. Causality is by context index, not by logical
+ * position. Pad tokens are ordinary tokens.
+ * Cache slots past ctx_len[r] in request r's last block hold no token: their
+ * K/V may be anything (unwritten memory, NaN); they never reach a result, and
+ * logical_pos entries past ctx_len[r] are not read for a result either (no
+ * MINIPIC_EW_POS for them).
  */
 typedef struct minipic_batch {
   int32_t num_reqs;            /* number of requests, >= 0 */
   int32_t num_q_heads;         /* Hq */
-  int32_t num_kv_heads;        /* Hkv; Hq / Hkv must be 1, 2, 4 or 8 */
+  int32_t num_kv_heads;        /* Hkv, at most 255; Hq / Hkv must be 1, 2, 4 or 8 */
   int32_t head_dim;            /* d: 64 or 128 */
   int32_t block_size;          /* tokens per cache block: must be 16 */
   int32_t max_blocks_per_req;  /* row stride of block_table / span_id / blk_flags */
@@ -162,7 +171,10 @@ int minipic_get_launch_info(const minipic_batch* batch, int32_t dtype, minipic_l
  *              query's own logical position t = pi(c)) unless MINIPIC_FLAG_ROTATE_Q.
  *   k_cache, v_cache : layouts of minipic_write_kv, holding UNROTATED keys.
  *   num_blocks : physical blocks in each cache.
- *   cos_sin  : float32 [max_pos][head_dim] as filled by minipic_rope_table.
+ *   cos_sin  : float32 [max_pos][head_dim] as filled by minipic_rope_table;
+ *              max_pos * head_dim * 4 must stay below 2^31 bytes (the kernels
+ *              address the table through a 32-bit buffer range), else
+ *              MINIPIC_ERR_INVALID_ARG.
  *   softmax_scale : <= 0 means 1/sqrt(head_dim).
  *   out      : [total_q][num_q_heads][head_dim], element type `dtype`.
  *   workspace: device scratch of minipic_workspace_size() bytes (256-byte

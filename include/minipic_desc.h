@@ -20,8 +20,11 @@
  * "Fast splittable pseudorandom number generators", 2014):
  *   h <- mix(h ^ token + 0x9E3779B97F4A7C15).
  * A GLOBAL marker (an extension for a Prompt-Cache prefix, not one of the
- * pages' three primitives) hashes like SSep and sets the GLOBAL flag on its
- * segment's blocks.
+ * pages' three primitives) sets the GLOBAL flag on its segment's blocks. Every
+ * later token attends to GLOBAL blocks, so the K/V of a span that follows a
+ * GLOBAL segment depend on it: a block that starts with SSep or GLOBAL hashes
+ * as H(g, x_i), where g is the hash of the last GLOBAL block before it (h_0
+ * when there is none). Without a GLOBAL segment this is the rule above.
  */
 #ifndef MINIPIC_DESC_H
 #define MINIPIC_DESC_H

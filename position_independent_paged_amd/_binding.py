@@ -75,11 +75,17 @@ class minipic_launch_info(ctypes.Structure):
 _lib = None
 
 
-def load_library(path: str = LIB_PATH):
-    """Load libminipic.so; fails loudly if it has not been built."""
+def load_library(path: str = None):
+    """Load libminipic.so; fails loudly if it has not been built.
+
+    MINIPIC_LIBRARY names another build of the same library (the tests load a
+    copy whose host code is built with address and undefined-behaviour
+    sanitizers this way)."""
     global _lib
     if _lib is not None:
         return _lib
+    if path is None:
+        path = os.environ.get("MINIPIC_LIBRARY") or LIB_PATH
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with `python -m position_independent_paged_amd.build`")
     lib = ctypes.CDLL(path)

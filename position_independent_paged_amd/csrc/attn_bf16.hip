@@ -123,6 +123,7 @@ struct Stage {
   uint32_t ka[CW / 2], kb[CW / 2];   // CW bf16 of each half of the K unit
   float c[CW], s[CW];                // cos / sin of the unit's CW frequencies
   u32x4 v[Cfg<D, RB>::VU];
+  int nv[Cfg<D, RB>::VU];            // keys inside the context in each V piece's block
 };
 
 // Per-pass state the step helpers need (all wave-uniform).
@@ -142,7 +143,7 @@ struct StepCtx {
 // The lane's query rows.
 template <int RB>
 struct RowInfo {
-  int c[RB], bq[RB], span[RB];
+  int c[RB], bq[RB], span[RB], lo[RB];
   bool valid[RB], pdep[RB];
 };
 
@@ -153,7 +154,7 @@ struct RowInfo {
 template <int D, int RB>
 struct Pre {
   int ph_k, pos;
-  int ph_v[Cfg<D, RB>::VU];
+  int ph_v[Cfg<D, RB>::VU], nv_v[Cfg<D, RB>::VU];
 };
 
 template <int D, int RB, bool ROPE>
@@ -168,7 +169,9 @@ __device__ __forceinline__ void prefetch(const StepCtx<D, RB>& cx, int jk, int j
   for (int u = 0; u < C::VU; ++u) {
     const int u0 = __builtin_amdgcn_readfirstlane(tid + u * C::NT);
     const bool act = (C::VU * C::NT == C::VUNITS) || u0 < C::VUNITS;
-    pr.ph_v[u] = act ? cx.lst[__builtin_amdgcn_readfirstlane(2 * jv + u0 / (2 * D))].phys : -1;
+    const int ev = __builtin_amdgcn_readfirstlane(2 * jv + u0 / (2 * D));
+    pr.ph_v[u] = act ? cx.lst[ev].phys : -1;
+    pr.nv_v[u] = act ? cx.lst[ev].nvalid : kBlock;
   }
 }
 
@@ -224,6 +227,7 @@ __device__ __forceinline__ void load_v(const StepCtx<D, RB>& cx, const Pre<D, RB
     const rsrc_t r = make_rsrc(cx.vc + (int64_t)(ph < 0 ? 0 : ph) * cx.group, ph >= 0 ? kBlock * D * 2 : 0);
     st.v[u] = __builtin_bit_cast(
         u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, ((rem / 2) * kBlock + 8 * (rem % 2)) * 2, 0, 0));
+    st.nv[u] = __builtin_amdgcn_readfirstlane(pr.nv_v[u]);
   }
 }
 
@@ -270,7 +274,18 @@ __device__ __forceinline__ void store_v(const StepCtx<D, RB>& cx, int buf, const
     if (C::VUNITS % C::NT != 0 && unit >= C::VUNITS) continue;
     const int bk = unit / (2 * D);
     const int rem = unit % (2 * D);
-    *(u32x4*)(cx.vl + buf * C::VSZ + (rem / 2) * C::VSTR + kBlock * bk + 8 * (rem % 2)) = st.v[u];
+    u32x4 val = st.v[u];
+    if (st.nv[u] < kBlock) {
+      // a ragged last block: its slots past the context hold no token (maybe
+      // NaN); P is 0 there, but 0 * NaN would still reach O, so zero them
+      const int k0 = 8 * (rem % 2);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int k = k0 + 2 * w;
+        val[w] = k >= st.nv[u] ? 0u : (k + 1 >= st.nv[u] ? (val[w] & 0xffffu) : val[w]);
+      }
+    }
+    *(u32x4*)(cx.vl + buf * C::VSZ + (rem / 2) * C::VSTR + kBlock * bk + 8 * (rem % 2)) = val;
   }
 }
 
@@ -332,8 +347,8 @@ __device__ __forceinline__ void apply_mask(const StepCtx<D, RB>& cx, int j, cons
     const BlkDesc bd = cx.lst[2 * j + bk];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      const bool vis = rows.valid[rb] &&
-                       block_visible(bd.kb, bd.span, bd.flags, rows.bq[rb], rows.span[rb], rows.pdep[rb]);
+      const bool vis = rows.valid[rb] && block_visible(bd.kb, bd.span, bd.flags, rows.bq[rb], rows.span[rb],
+                                                       rows.pdep[rb], rows.lo[rb]);
       const int lim = rows.c[rb] - bd.kb * kBlock - 8 * h;
 #pragma unroll
       for (int r = 0; r < 8; ++r)
@@ -531,8 +546,10 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
                 pd[q] = u32x4{(uint32_t)(pos0 + 4 * q), (uint32_t)(pos0 + 4 * q + 1), (uint32_t)(pos0 + 4 * q + 2),
                               (uint32_t)(pos0 + 4 * q + 3)};
             } else {
+              const int nvalid = (int)bdv[k][1][2];
               for (int o2 = 0; o2 < kBlock; ++o2) {
-                int pos = lpos[kb * kBlock + o2];
+                // keys past the context hold no token: any row of the table will do
+                int pos = o2 < nvalid ? lpos[kb * kBlock + o2] : 0;
                 if (pos < 0 || pos >= P.max_pos) {
                   atomicOr(&P.hdr->err, (uint32_t)MINIPIC_EW_POS);
                   pos = pos < 0 ? 0 : P.max_pos - 1;
@@ -591,6 +608,7 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
       rows.c[rb] = valid ? tk.c : -1;
       rows.bq[rb] = valid ? (tk.c >> 4) : -1;
       rows.span[rb] = tk.span;
+      rows.lo[rb] = tk.lo;
       rows.pdep[rb] = valid && tk.pdep;
     }
     // the claim is issued after the list and q loads: loads retire in issue

@@ -54,6 +54,7 @@ __global__ void __launch_bounds__(kNTf) attn_f32_kernel(AttnParams P) {
     const int c_row = rvalid ? tk.c : -1;
     const int bq_row = rvalid ? (c_row >> 4) : -1;
     const int span_row = tk.span;
+    const int lo_row = tk.lo;
     const bool pdep_row = rvalid && tk.pdep;
     const int head = g * G + hig;
     const int64_t qrow = (int64_t)item.row0 + tok;
@@ -105,7 +106,8 @@ __global__ void __launch_bounds__(kNTf) attn_f32_kernel(AttnParams P) {
             a = kr[i];
             b = kr[i + D / 2];
             if (ROPE) {
-              int pos = bd.pos0 >= 0 ? bd.pos0 + key : lpos[bd.kb * kBlock + key];
+              // a key past the context holds no token (never visible): any table row will do
+              int pos = key >= bd.nvalid ? 0 : (bd.pos0 >= 0 ? bd.pos0 + key : lpos[bd.kb * kBlock + key]);
               if (pos < 0 || pos >= P.max_pos) {
                 atomicOr(&P.hdr->err, (uint32_t)MINIPIC_EW_POS);
                 pos = pos < 0 ? 0 : P.max_pos - 1;
@@ -127,7 +129,7 @@ __global__ void __launch_bounds__(kNTf) attn_f32_kernel(AttnParams P) {
           vt[key][d] = bd.phys >= 0 ? vc[(((int64_t)bd.phys * P.hkv + g) * D + d) * kBlock + key] : 0.f;
         }
         __syncthreads();
-        const bool vis = rvalid && block_visible(bd.kb, bd.span, bd.flags, bq_row, span_row, pdep_row);
+        const bool vis = rvalid && block_visible(bd.kb, bd.span, bd.flags, bq_row, span_row, pdep_row, lo_row);
         for (int key = 0; key < kBlock; ++key) {
           float dot = 0.f;
 #pragma unroll

@@ -23,11 +23,17 @@
 // a key at context index j:
 //     visible(c, j) = j <= c and (PDEP(c's block) or GLOBAL(j's block)
 //                                 or span(j's block) == span(c's block))
-// Under the contract that one span id names one contiguous run of blocks, the
-// key blocks a tile may see are the GLOBAL blocks below `lo` plus blocks of
-// [lo, hi], where hi is the block of the tile's last query and lo is 0 if a
-// row is PDep, else the start of the run holding the tile's first query.
-// plan_tiles keeps the blocks of that range some row really sees.
+// The span test compares runs, not bare ids: a span id names one contiguous
+// run of blocks (the caller's contract), and a block with the row's span id
+// that lies before the start of the row's own run is a different, invisible
+// span. plan_tiles records each row's run start, sets MINIPIC_EW_SPAN in the
+// error word when such an earlier block exists (the contract is broken), and
+// the attention kernels evaluate the same run-based rule, so the result never
+// depends on how rows are grouped into tiles.
+// The key blocks a tile may see are then the GLOBAL blocks below `lo` plus
+// blocks of [lo, hi], where hi is the block of the tile's last query and lo
+// is 0 if a row is PDep, else the earliest run start of its rows. plan_tiles
+// keeps the blocks of that range some row really sees.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -98,7 +104,7 @@ struct TokDesc {
   int32_t c;       // context index, -1 for a row past the end of the tile
   int32_t span;    // span id of its block
   int32_t pdep;    // PDEP bit of its block
-  int32_t pad;
+  int32_t lo;      // first block of the run of its span id that holds its block (0 for PDep rows)
 };
 
 // One visible key block of a tile.
@@ -112,7 +118,9 @@ struct BlkDesc {
                    // each key's position up in logical_pos
   int32_t full;    // 1: every query row of the tile sees every key of the block (the
                    // block lies below each row's own block and is visible to each row)
-  int32_t pad1, pad2;
+  int32_t nvalid;  // keys of the block inside the context (16 except in a ragged last block);
+                   // keys past it hold no token: their values are never read into a result
+  int32_t pad2;
 };
 
 // One unit of attention work: KV head g of tile `tile`, list entries [p0, p1),
@@ -262,10 +270,12 @@ __device__ __forceinline__ int block_excl_scan_pred(bool pred, int* tmp, int* to
 }
 
 // Block-level visibility of key block (kb, span, flags) for a query row in
-// block bq with (span_row, pdep_row); the causal test inside the diagonal
-// block is element-wise and done by the caller.
-__device__ __forceinline__ bool block_visible(int kb, int span, int flags, int bq, int span_row, bool pdep_row) {
-  return kb <= bq && (pdep_row || (flags & MINIPIC_BLK_GLOBAL) || span == span_row);
+// block bq with (span_row, pdep_row) whose span run starts at block lo_row;
+// the causal test inside the diagonal block is element-wise and done by the
+// caller.
+__device__ __forceinline__ bool block_visible(int kb, int span, int flags, int bq, int span_row, bool pdep_row,
+                                              int lo_row) {
+  return kb <= bq && (pdep_row || (flags & MINIPIC_BLK_GLOBAL) || (span == span_row && kb >= lo_row));
 }
 
 // Work items are claimed with one atomic add on the counter of the queue the

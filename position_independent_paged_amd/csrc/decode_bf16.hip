@@ -75,6 +75,21 @@ __global__ void __launch_bounds__(64) decode_bf16_kernel(DecodeParams P) {
   if (L > 0 && b0 < b1) {
     const int span_q = span[bq];
     const bool pdep_q = (flg[bq] & MINIPIC_BLK_PDEP) != 0;
+    // first block of the query's span run (the span test compares runs; a
+    // block with the query's span id before it breaks the span-id contract)
+    int lo_q = 0;
+    if (!pdep_q) {
+      int base = bq;
+      while (true) {
+        const int b2 = base - 1 - l;
+        const uint64_t sb = __ballot(b2 < 0 || span[b2] != span_q);
+        if (sb) {
+          lo_q = base - (__ffsll((unsigned long long)sb) - 1);
+          break;
+        }
+        base -= 64;
+      }
+    }
     // Q^T operand: lane (n, j) holds d = 32 t + 8 j + [0, 8) of query head g G + n
     bf16x8 qf[NC];
     {
@@ -103,8 +118,12 @@ __global__ void __launch_bounds__(64) decode_bf16_kernel(DecodeParams P) {
     }
     // the next block of the split the query sees, or b1
     auto next_visible = [&](int b) {
-      for (; b < b1; ++b)
-        if (pdep_q || (flg[b] & MINIPIC_BLK_GLOBAL) || span[b] == span_q) break;
+      for (; b < b1; ++b) {
+        const bool glob = (flg[b] & MINIPIC_BLK_GLOBAL) != 0;
+        const bool same = span[b] == span_q;
+        if (!pdep_q && !glob && same && b < lo_q && l == 0 && g == 0) atomicOr(P.err, (uint32_t)MINIPIC_EW_SPAN);
+        if (pdep_q || glob || (same && b >= lo_q)) break;
+      }
       return b;
     };
     // K rows: lane (n, j) = key n of the block, d slices 8 j of every chunk;
@@ -129,7 +148,9 @@ __global__ void __launch_bounds__(64) decode_bf16_kernel(DecodeParams P) {
 #pragma unroll
         for (int mt = 0; mt < NM; ++mt) va[mt] = s16x4{0, 0, 0, 0};
       }
-      pos = ROPE ? lpos[b * kBlock + n] : 0;
+      // a key past the context holds no token: its position is not read (the
+      // lane then follows the block's run of positions, or reads row 0)
+      pos = ROPE && b * kBlock + n < L ? lpos[b * kBlock + n] : 0;
     };
     // one block in flight ahead of the one being computed
     bf16x8 ka_n[NC];
@@ -151,7 +172,8 @@ __global__ void __launch_bounds__(64) decode_bf16_kernel(DecodeParams P) {
       if (ROPE) {
         // rotate-half at the key's logical position: element i (first half)
         // with element i + D/2, in fp32, one rounding to bf16
-        if (pos < 0 || pos >= P.max_pos) {
+        const bool past = bc * kBlock + n >= L;   // lane 0 (key 0) never is
+        if (!past && (pos < 0 || pos >= P.max_pos)) {
           atomicOr(P.err, (uint32_t)MINIPIC_EW_POS);
           pos = pos < 0 ? 0 : P.max_pos - 1;
         }
@@ -159,7 +181,7 @@ __global__ void __launch_bounds__(64) decode_bf16_kernel(DecodeParams P) {
         // p0, shared by the block's 16 keys, and add the angle n theta_i;
         // otherwise read each key's own row
         const int p0 = __builtin_amdgcn_readfirstlane(pos);   // lane 0 holds key 0
-        const bool cons = delta_ok && __all(pos == p0 + n);
+        const bool cons = delta_ok && __all(past || pos == p0 + n);
         const float* cs = P.cos_sin + (int64_t)(cons ? p0 : pos) * D + 8 * j;
 #pragma unroll
         for (int t = 0; t < NH; ++t) {
@@ -221,6 +243,16 @@ __global__ void __launch_bounds__(64) decode_bf16_kernel(DecodeParams P) {
       // the row sum of the bf16 values the numerator uses
       l_run += (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
       const s16x4 pb = __builtin_bit_cast(s16x4, u32x2{p01, p23});
+      if (bc == bq) {
+        // keys after the query: P is 0, and slots past the context may hold
+        // anything (NaN) that 0 * V would still carry into O; zero them
+        const int lim = c - bq * kBlock - 4 * j;
+#pragma unroll
+        for (int mt = 0; mt < NM; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (i > lim) va[mt][i] = 0;
+      }
       // ---- O^T += V^T P^T
 #pragma unroll
       for (int mt = 0; mt < NM; ++mt) o[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[mt], pb, o[mt], 0, 0, 0);

@@ -67,6 +67,12 @@ int minipic_describe_blocks(const int32_t* tokens, int64_t n, const minipic_mark
   }
   uint64_t h_prev = m->seed;   // h_{i-1}
   uint64_t g = m->seed;        // H(h_0, x_<=i): every token so far
+  // Hash of the last GLOBAL block so far (h_0 before the first). Tokens of a
+  // span attend to every earlier GLOBAL block, so from the second layer on
+  // their K/V depend on that prefix: a span (or a later GLOBAL segment)
+  // chains from it instead of h_0, and the same document after a different
+  // shared prefix does not hit.
+  uint64_t anchor = m->seed;
   int32_t span = 0;
   uint8_t seg_flags = 0;
   for (int64_t i = 0; i < nb; ++i) {
@@ -75,7 +81,7 @@ int minipic_describe_blocks(const int32_t* tokens, int64_t n, const minipic_mark
     g = fold(g, x, len);
     uint64_t h;
     if (is(x[0], m->ssep) || is(x[0], m->global_)) {
-      h = fold(m->seed, x, len);
+      h = fold(anchor, x, len);
     } else if (is(x[0], m->pdep)) {
       h = g;
     } else {
@@ -89,6 +95,7 @@ int minipic_describe_blocks(const int32_t* tokens, int64_t n, const minipic_mark
     span_id[i] = span;
     flags[i] = seg_flags;
     h_prev = h;
+    if (seg_flags & MINIPIC_BLK_GLOBAL) anchor = h;
   }
   *num_blocks = nb;
   return MINIPIC_OK;

@@ -71,6 +71,8 @@ int check_batch(const minipic_batch* b, int dtype) {
   if (b->num_reqs < 0) return fail(MINIPIC_ERR_INVALID_ARG, "num_reqs < 0");
   if (b->num_q_heads <= 0 || b->num_kv_heads <= 0)
     return fail(MINIPIC_ERR_INVALID_ARG, "head counts must be positive");
+  if (b->num_kv_heads > 255)   // work items pack the KV head into 8 bits
+    return fail(MINIPIC_ERR_UNSUPPORTED, "num_kv_heads must be at most 255 (got %d)", b->num_kv_heads);
   if (b->num_q_heads % b->num_kv_heads != 0)
     return fail(MINIPIC_ERR_UNSUPPORTED, "num_q_heads %% num_kv_heads != 0");
   if (!supported_group(b->num_q_heads / b->num_kv_heads))
@@ -91,6 +93,15 @@ int check_batch(const minipic_batch* b, int dtype) {
   }
   if (b->total_q > (int64_t)INT32_MAX) return fail(MINIPIC_ERR_INVALID_ARG, "total_q too large");
   if ((uintptr_t)b->logical_pos % 16) return fail(MINIPIC_ERR_INVALID_ARG, "logical_pos must be 16-byte aligned");
+  return MINIPIC_OK;
+}
+
+// The kernels address the cos/sin table through a buffer range of 32-bit size.
+int check_table(const float* cos_sin, int32_t max_pos, int head_dim) {
+  if (!cos_sin) return fail(MINIPIC_ERR_INVALID_ARG, "cos_sin is NULL");
+  if (max_pos <= 0) return fail(MINIPIC_ERR_INVALID_ARG, "max_pos must be > 0");
+  if ((int64_t)max_pos * head_dim * (int64_t)sizeof(float) > (int64_t)INT32_MAX)
+    return fail(MINIPIC_ERR_INVALID_ARG, "cos/sin table of %d rows x %d floats exceeds 2^31 bytes", max_pos, head_dim);
   return MINIPIC_OK;
 }
 
@@ -164,8 +175,8 @@ int run_decode(const void* q, const void* k_cache, const void* v_cache, int64_t 
   if (flags) return fail(MINIPIC_ERR_INVALID_ARG, "decode takes no flags (q arrives rotated), got 0x%x", flags);
   if (num_blocks < 0) return fail(MINIPIC_ERR_INVALID_ARG, "num_blocks < 0");
   if (rope) {
-    if (!cos_sin) return fail(MINIPIC_ERR_INVALID_ARG, "cos_sin is NULL");
-    if (max_pos <= 0) return fail(MINIPIC_ERR_INVALID_ARG, "max_pos must be > 0");
+    st = check_table(cos_sin, max_pos, b->head_dim);
+    if (st) return st;
   }
   if (b->num_reqs == 0) return MINIPIC_OK;
   if (!q || !out) return fail(MINIPIC_ERR_INVALID_ARG, "q or out is NULL");
@@ -244,7 +255,11 @@ void make_plan(const minipic_batch* b, int dtype, Plan* p) {
   if (p->min_chunk < 1) p->min_chunk = 1;
   const int64_t hkv = b->num_kv_heads;
   int64_t slots = p->tiles * hkv * kMaxSplits;
-  if (slots > kSlotCap) slots = kSlotCap;
+  // MINIPIC_SLOT_CAP lowers the cap (tuning and tests of the planner's
+  // piece-doubling path); it never raises it past the workspace plan
+  int cap = env_int("MINIPIC_SLOT_CAP", kSlotCap);
+  if (cap < 2 || cap > kSlotCap) cap = kSlotCap;
+  if (slots > cap) slots = cap;
   p->slots = (int)slots;
   p->max_items = p->tiles * hkv + p->slots;
   size_t off = kAlign;  // WsHeader
@@ -301,8 +316,8 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, int64
   if (num_blocks < 0) return fail(MINIPIC_ERR_INVALID_ARG, "num_blocks < 0");
   const bool need_table = rope || (flags & MINIPIC_FLAG_ROTATE_Q);
   if (need_table) {
-    if (!cos_sin) return fail(MINIPIC_ERR_INVALID_ARG, "cos_sin is NULL");
-    if (max_pos <= 0) return fail(MINIPIC_ERR_INVALID_ARG, "max_pos must be > 0");
+    st = check_table(cos_sin, max_pos, b->head_dim);
+    if (st) return st;
   }
   if (b->num_reqs == 0 || b->total_q == 0) return MINIPIC_OK;
   if (!q || !out) return fail(MINIPIC_ERR_INVALID_ARG, "q or out is NULL");

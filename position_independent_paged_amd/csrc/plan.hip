@@ -19,9 +19,10 @@
 namespace minipic {
 
 // Descriptor of one listed key block. `lpos` is the request's row of logical
-// positions, `L` its context length. pos0 is set when the block's positions
-// (those of its tokens below L) run pos0, pos0+1, ... and the whole run
-// pos0 .. pos0+15 lies inside the cos/sin table.
+// positions, `L` its context length. Only the block's keys below L hold
+// tokens (nvalid of them): pos0 is set when their positions run pos0, pos0+1,
+// ... and all of them lie inside the cos/sin table; positions past L are
+// never read for a result.
 __device__ __forceinline__ BlkDesc blk_from(const PlanParams& P, int ph, const int4 (&pp)[kBlock / 4], int L, int kb,
                                             int span, int flags, int full) {
   if (ph < 0 || (int64_t)ph >= P.num_blocks) {
@@ -36,11 +37,11 @@ __device__ __forceinline__ BlkDesc blk_from(const PlanParams& P, int ph, const i
     p[4 * i + 2] = pp[i].z;
     p[4 * i + 3] = pp[i].w;
   }
-  const int nvalid = min(kBlock, L - kb * kBlock);
-  bool cons = p[0] >= 0 && p[0] <= P.max_pos - kBlock;
+  const int nvalid = max(0, min(kBlock, L - kb * kBlock));
+  bool cons = p[0] >= 0 && p[0] <= P.max_pos - nvalid;
 #pragma unroll
   for (int k = 1; k < kBlock; ++k) cons = cons && (k >= nvalid || p[k] == p[0] + k);
-  return BlkDesc{kb, ph, span, flags, cons ? p[0] : -1, full, 0, 0};
+  return BlkDesc{kb, ph, span, flags, cons ? p[0] : -1, full, nvalid, 0};
 }
 
 __device__ __forceinline__ BlkDesc make_blk(const PlanParams& P, int ph, const int32_t* lpos, int L, int kb, int span,
@@ -58,7 +59,7 @@ __global__ void __launch_bounds__(NT) plan_tiles_kernel(PlanParams P) {
   constexpr int BPT = kPlanBlocksPerThread;
   constexpr int PASS = NT * BPT;   // key blocks per pass, each thread owning BPT consecutive ones
   __shared__ int qblk[BQ];
-  __shared__ int e_bq[BQ], e_span[BQ], e_pdep[BQ];
+  __shared__ int e_bq[BQ], e_span[BQ], e_pdep[BQ], e_lo[BQ];
   __shared__ int tmp[NT / 64];
   __shared__ int s_hi, s_lo, s_anyp, s_phi;
   __shared__ int s_span[PASS];     // span ids and flags of the first pass's blocks
@@ -133,10 +134,7 @@ __global__ void __launch_bounds__(NT) plan_tiles_kernel(PlanParams P) {
     sp = span_at(bq);
     pd = (flg_at(bq) & MINIPIC_BLK_PDEP) ? 1 : 0;
   }
-  if (tid < BQ) {
-    P.toks[(int64_t)t * BQ + tid] = TokDesc{valid ? c : -1, sp, pd, 0};
-    qblk[tid] = bq;
-  }
+  if (tid < BQ) qblk[tid] = bq;
   __syncthreads();
 
   // ---- distinct query blocks ("entries")
@@ -150,58 +148,89 @@ __global__ void __launch_bounds__(NT) plan_tiles_kernel(PlanParams P) {
   }
   __syncthreads();
 
-  // ---- key range (wave 0)
+  // ---- run start of every non-PDep entry (wave 0): the first block of the
+  // run of equal span ids that holds the entry's block. An entry in the block
+  // right after the previous entry's, with the same span id, shares that
+  // entry's run; every other entry searches backwards, 64 blocks per round.
   if (tid < 64) {
-    int hi = -1, mn = INT_MAX, anyp = 0, phi = -1;
+    int carry = 0;   // run start of the last searched entry of earlier chunks
+    for (int e0 = 0; e0 < n_e; e0 += 64) {
+      const int e = e0 + lane;
+      bool need = false;
+      if (e < n_e && !e_pdep[e])
+        need = e == 0 || e_pdep[e - 1] || e_span[e] != e_span[e - 1] || e_bq[e] != e_bq[e - 1] + 1;
+      const uint64_t nm = __ballot(need);
+      uint64_t m = nm;
+      int my_lo = 0;
+      while (m) {
+        const int k = __ffsll((unsigned long long)m) - 1;
+        m &= m - 1;
+        const int sm = e_span[e0 + k];
+        int base = e_bq[e0 + k];
+        int start;
+        while (true) {
+          const int b2 = base - 1 - lane;
+          const bool stop = (b2 < 0) || (span_at(b2) != sm);
+          const uint64_t sb = __ballot(stop);
+          if (sb) {
+            start = base - (__ffsll((unsigned long long)sb) - 1);
+            break;
+          }
+          base -= 64;
+        }
+        if (lane == k) my_lo = start;
+      }
+      // an entry that shares a run takes the start of the nearest searched entry before it
+      const uint64_t upto = nm & (lane == 63 ? ~0ull : ((2ull << lane) - 1));
+      const int src = upto ? 63 - __clzll((long long)upto) : -1;
+      const int inherited = __shfl(my_lo, src < 0 ? 0 : src, 64);
+      const int lo_e = need ? my_lo : (src >= 0 ? inherited : carry);
+      if (e < n_e) e_lo[e] = e_pdep[e] ? 0 : lo_e;
+      if (nm) carry = __shfl(my_lo, 63 - __clzll((long long)nm), 64);
+    }
+  }
+  __syncthreads();
+  if (tid < BQ) P.toks[(int64_t)t * BQ + tid] = TokDesc{valid ? c : -1, sp, pd, valid ? e_lo[idx - (first ? 0 : 1)] : 0};
+
+  // ---- key range (wave 0): lo = 0 if some row is PDep, else the earliest run start
+  if (tid < 64) {
+    int hi = -1, lo = INT_MAX, anyp = 0, phi = -1;
     for (int e = lane; e < n_e; e += 64) {
-      const int b = e_bq[e];
-      hi = max(hi, b);
-      mn = min(mn, b);
+      const int b2 = e_bq[e];
+      hi = max(hi, b2);
+      lo = min(lo, e_lo[e]);
       if (e_pdep[e]) {
         anyp = 1;
-        phi = max(phi, b);
+        phi = max(phi, b2);
       }
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
       hi = max(hi, __shfl_xor(hi, o, 64));
-      mn = min(mn, __shfl_xor(mn, o, 64));
+      lo = min(lo, __shfl_xor(lo, o, 64));
       anyp |= __shfl_xor(anyp, o, 64);
       phi = max(phi, __shfl_xor(phi, o, 64));
     }
-    // start of the run of equal span ids that holds the smallest query block
-    int lo = 0;
-    if (!anyp && mn != INT_MAX) {
-      const int sm = span_at(mn);
-      int base = mn;
-      while (true) {
-        const int b = base - 1 - lane;
-        const bool stop = (b < 0) || (span_at(b) != sm);
-        const uint64_t m = __ballot(stop);
-        if (m) {
-          lo = base - (__ffsll((unsigned long long)m) - 1);
-          break;
-        }
-        base -= 64;
-      }
-    }
     if (lane == 0) {
       s_hi = hi;
-      s_lo = lo;
+      s_lo = (anyp || lo == INT_MAX) ? 0 : lo;
       s_anyp = anyp;
       s_phi = phi;
     }
   }
   __syncthreads();
-  const int lo = s_lo, hi = s_hi, anyp = s_anyp, phi = s_phi;
+  const int lo = s_lo, hi = s_hi;
 
   // ---- compacted list, in block order: the GLOBAL blocks below lo (visible
   // to every row, below every query block) and the blocks of [lo, hi] some row
   // sees. A pass covers PASS blocks, each thread owning BPT consecutive ones,
   // so all loads of a pass are in flight together (the first pass's were
-  // loaded at the start) and one scan places the visible blocks.
+  // loaded at the start) and one scan places the visible blocks. A block that
+  // carries a row's span id before the row's own run breaks the span-id
+  // contract: it is not visible to that row, and the error word says so.
   BlkDesc* out = P.blist + (int64_t)t * P.max_blocks;
   int n = 0;
+  bool broken = false;
   for (int base = 0; base <= hi; base += PASS) {
     int f[BPT], s[BPT];
     bool vis[BPT], full[BPT];
@@ -216,16 +245,17 @@ __global__ void __launch_bounds__(NT) plan_tiles_kernel(PlanParams P) {
       if (kb <= hi) {
         f[j] = base == 0 ? f0[j] : flg[kb];
         s[j] = base == 0 ? s0[j] : span[kb];
-        if (kb < lo) {
-          vis[j] = (f[j] & MINIPIC_BLK_GLOBAL) != 0;
-        } else {
-          // visible to some row (vis) / to every row, strictly below its own block (full)
-          for (int e = 0; e < n_e; ++e) {
-            const bool see = kb <= e_bq[e] && (e_pdep[e] || (f[j] & MINIPIC_BLK_GLOBAL) || e_span[e] == s[j]);
-            vis[j] = vis[j] || see;
-            full[j] = full[j] && see && kb < e_bq[e];
-          }
+        const bool glob = (f[j] & MINIPIC_BLK_GLOBAL) != 0;
+        // visible to some row (vis) / to every row, strictly below its own block (full)
+        for (int e = 0; e < n_e; ++e) {
+          const bool same = e_span[e] == s[j];
+          const bool in_run = kb >= e_lo[e];
+          const bool see = kb <= e_bq[e] && (e_pdep[e] || glob || (same && in_run));
+          broken = broken || (same && !in_run && !glob);
+          vis[j] = vis[j] || see;
+          full[j] = full[j] && see && kb < e_bq[e];
         }
+        vis[j] = vis[j] && (kb >= lo || glob);
       }
       cnt += vis[j] ? 1 : 0;
     }
@@ -239,6 +269,7 @@ __global__ void __launch_bounds__(NT) plan_tiles_kernel(PlanParams P) {
       }
     n += tot;
   }
+  if (broken) atomicOr(&P.hdr->err, (uint32_t)MINIPIC_EW_SPAN);
   if (tid == 0) *td = TileDesc{r, row0, nq, n, 0, -1, 0, 0};
 }
 

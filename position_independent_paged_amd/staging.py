@@ -67,7 +67,7 @@ class DeviceWorkload:
     ``attend`` runs the attention of the step.
     """
 
-    def __init__(self, w, device="cuda", rope_table=True, flags=0):
+    def __init__(self, w, device="cuda", rope_table=True, flags=0, cache_fill=0.0):
         self.w = w
         self.device = device
         self.dtype_code = MINIPIC_BF16 if w.dtype == "bf16" else MINIPIC_F32
@@ -78,8 +78,10 @@ class DeviceWorkload:
                                  blk_flags=w.blk_flags, num_q_heads=w.num_q_heads, num_kv_heads=Hkv,
                                  head_dim=D, block_size=B, device=device)
         self.num_blocks = int(w.num_blocks)
-        self.k_cache = torch.zeros((self.num_blocks, Hkv, B, D), dtype=tdt, device=device)
-        self.v_cache = torch.zeros((self.num_blocks, Hkv, D, B), dtype=tdt, device=device)
+        # cache_fill: the value of every slot no token is written to (NaN
+        # stands for unwritten or recycled memory)
+        self.k_cache = torch.full((self.num_blocks, Hkv, B, D), cache_fill, dtype=tdt, device=device)
+        self.v_cache = torch.full((self.num_blocks, Hkv, D, B), cache_fill, dtype=tdt, device=device)
         self.q = _values(w.q, w.dtype, device)
         self.out = torch.zeros_like(self.q)
         self.k_new = _values(w.k_tok[w.new_tok], w.dtype, device)

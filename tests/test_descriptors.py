@@ -180,3 +180,31 @@ def test_block_cache_full_records_nothing():
     h2, _, _ = describe(doc(rng, 48))                 # 3 blocks fit: nothing was taken before
     bt, hit, n = cache.assign(h2)
     assert n == 0 and sorted(bt.tolist()) == [0, 1, 2]
+
+
+def test_document_after_a_shared_prefix_chains_from_it():
+    """A span's tokens attend to every earlier GLOBAL block, so its K/V depend
+    on that prefix: the same document after two different GLOBAL prefixes
+    must not share cache blocks, after the same prefix it must, and without a
+    GLOBAL segment the SSep rule (hash from h_0) is unchanged."""
+    rng = np.random.default_rng(9)
+    pre_a, pre_b = doc(rng, 64, marker=GLOB), doc(rng, 64, marker=GLOB)
+    d = doc(rng, 80)
+    task = doc(rng, 20, PDEP)
+    npre, nd = len(pre_a) // 16, len(d) // 16
+    ha, _, fa = describe(pre_a + d + task)
+    hb, _, _ = describe(pre_b + d + task)
+    hc, _, _ = describe(pre_a + doc(rng, 32) + d + task)      # same prefix, the document later
+    h0, _, _ = describe(d)                                     # no prefix: SSep hashes from h_0
+    doc_a, doc_b = ha[npre:npre + nd], hb[npre:npre + nd]
+    assert np.all(doc_a != doc_b)
+    assert np.array_equal(hc[npre + 2:npre + 2 + nd], doc_a)
+    assert np.all(doc_a != h0)
+    assert np.all(fa[:npre] == pip.MINIPIC_BLK_GLOBAL) and np.all(fa[npre:npre + nd] == 0)
+    cache = pip.BlockCache(64)
+    _, _, n1 = cache.assign(ha)
+    _, hit_b, n2 = cache.assign(hb)
+    assert n1 == 0 and n2 == 0 and not hit_b.any()
+    _, hit_c, _ = cache.assign(hc)
+    assert np.all(hit_c[:npre] == 1) and np.all(hit_c[npre + 2:npre + 2 + nd] == 1)
+    cache.close()

@@ -153,17 +153,92 @@ def test_parity_all_rows(name):
     check(name, got, want, w.dtype)
 
 
-@pytest.mark.parametrize("name,rows", [("c4", 384), ("c5", 96), ("e4", 384)])
-def test_parity_sampled_full_size(name, rows):
+def check_full(name, got, want):
+    """bf16 bar at full size: max abs <= 2e-2 and rel-L2 <= 1e-2 against the
+    oracle. An output of magnitude 4 or more is stored in bf16 with a spacing
+    of 2^-5, so its rounding alone can reach 1.6e-2; where the max abs bar is
+    exceeded, the comparison is repeated against the oracle rounded to bf16 (the
+    output type), which must then meet the same 2e-2."""
+    err = np.abs(got - want)
+    mx = float(err.max())
+    rel = float(np.linalg.norm(got - want) / np.linalg.norm(want))
+    i = np.unravel_index(int(np.argmax(err)), err.shape)
+    say(f"  {name}: rows={got.shape[0]} max_abs={mx:.3e} (|want| there {abs(want[i]):.3f}) rel_l2={rel:.3e}")
+    assert np.isfinite(got).all(), name
+    assert rel <= 1e-2, (name, rel)
+    if mx > 2e-2:
+        want_b = workload.bf16_bits_to_f32(workload.f32_to_bf16_bits(want.astype(np.float32))).astype(np.float64)
+        mx_b = float(np.abs(got - want_b).max())
+        say(f"  {name}: max_abs against the oracle rounded to bf16 = {mx_b:.3e}")
+        assert mx_b <= 2e-2, (name, mx, mx_b)
+
+
+def full_size_rows(w, r, rng, sample):
+    """Rows of request r to compare: every PDep row, every row of one seeded
+    span segment with queries, and a seeded sample of the rest."""
+    q0, q1 = int(w.q_indptr[r]), int(w.q_indptr[r + 1])
+    qc = w.q_ctx_idx[q0:q1]
+    pdep = (w.blk_flags[r, qc // 16] & workload.FLAG_PDEP) != 0
+    pick = pdep.copy()
+    spans = [(s0, seg.length) for s0, seg in zip(w.seg_start[r], w.segments[r])
+             if seg.kind == "span" and seg.fresh and seg.pool is None]
+    if spans:
+        s0, n = spans[int(rng.integers(len(spans)))]
+        pick |= (qc >= s0) & (qc < s0 + n)
+    rest = np.nonzero(~pick)[0]
+    if len(rest):
+        pick[rng.choice(rest, size=min(sample, len(rest)), replace=False)] = True
+    return np.nonzero(pick)[0]
+
+
+@pytest.mark.parametrize("name,sample", [("c4", 128), ("c5", 32), ("e4", 0)])
+def test_parity_full_size(name, sample):
+    """The full benchmark layouts in the configuration bench.py times: every
+    PDep row (the long-context rows, split and merged), one whole span
+    segment per request, and a sample of the other rows."""
     w = workload.make_config(name)
-    say(f"parity(sampled) {name}: total_q={w.total_q} max_ctx={w.max_ctx_len}")
+    say(f"parity(full size) {name}: total_q={w.total_q} max_ctx={w.max_ctx_len}")
     dw = stage(w)
     say(f"  plan {dw.launch_info()}")
     dw.step()
     torch.cuda.synchronize()
     assert dw.error_word() == 0
-    got, want = compare_workload(w, out_f64(dw.out), rows_per_req=rows, seed=1)
-    check(name, got, want, w.dtype)
+    out = out_f64(dw.out)
+    rng = np.random.default_rng(1)
+    got, want = [], []
+    for r in range(w.num_reqs):
+        rows = full_size_rows(w, r, rng, sample)
+        q0 = int(w.q_indptr[r])
+        want.append(oracle.workload_reference(w, r, rows=rows))
+        got.append(out[q0 + rows])
+    check_full(name, np.concatenate(got), np.concatenate(want))
+
+
+def _sweep_layout(kind):
+    if kind == "causal16k":
+        return workload.custom("causal16k", [[Segment("pdep", 16384)]], num_q_heads=32, num_kv_heads=8,
+                               head_dim=128, dtype="bf16", rope_theta=5e5, max_pos=32768, seed=16)
+    return workload.custom("docs32", [[Segment("span", 1008) for _ in range(32)]], num_q_heads=32,
+                           num_kv_heads=8, head_dim=128, dtype="bf16", rope_theta=5e5, max_pos=32768, seed=32)
+
+
+@pytest.mark.parametrize("kind", ["causal16k", "docs32"])
+def test_parity_sweep_sizes(kind):
+    """Layouts of the preload sweeps at their own sizes: one 16K-token causal
+    prompt (every row PDep, the last q tile included) and 32 documents of 1008
+    tokens prefilled together as SSep spans."""
+    w = _sweep_layout(kind)
+    say(f"parity(sweep size) {kind}: total_q={w.total_q}")
+    dw = stage(w)
+    say(f"  plan {dw.launch_info()}")
+    dw.step()
+    torch.cuda.synchronize()
+    assert dw.error_word() == 0
+    rng = np.random.default_rng(2)
+    n = int(w.total_q)
+    rows = np.unique(np.concatenate([np.arange(n - 64, n), rng.choice(n - 64, size=96, replace=False)]))
+    want = oracle.workload_reference(w, 0, rows=rows)
+    check_full(kind, out_f64(dw.out)[rows], want)
 
 
 @pytest.mark.parametrize("name", ["c1", "c3_small", "c5_small"])

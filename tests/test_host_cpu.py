@@ -72,6 +72,7 @@ def _attn(b, dtype=1, ws_bytes=1 << 30, q=256, out=256, ws=256, table=256, max_p
     (dict(q_indptr=None), -1),
     (dict(max_q_len=0), -1),
     (dict(logical_pos=256 + 4), -1),                 # not 16-byte aligned
+    (dict(num_q_heads=256, num_kv_heads=256), -2),   # work items hold the KV head in 8 bits
 ])
 def test_attention_rejects_bad_batch(kw, code):
     assert _attn(_batch(**kw)) == code
@@ -88,6 +89,10 @@ def test_attention_rejects_bad_buffers():
     assert _attn(b, ws=None) == -1
     assert _attn(b, ws=256 + 4) == -1                 # misaligned
     assert _attn(b, ws_bytes=64) == -3
+    # the kernels address the cos/sin table through a 32-bit buffer range
+    assert _attn(b, max_pos=(1 << 22)) == -1          # 2^22 rows x 128 floats = 2^31 bytes
+    assert b"2^31" in pip.load_library().minipic_last_error()
+    assert _attn(b, max_pos=(1 << 22) - 1, ws_bytes=64) == -3
     # the pre-rotated variant does not need the table
     assert _attn(b, table=None, max_pos=0, ws_bytes=64, rope=False) == -3
 
@@ -113,6 +118,7 @@ def test_decode_validation():
     assert _decode(lib, _batch(**one), flags=pip.MINIPIC_FLAG_ROTATE_Q) == -1
     assert _decode(lib, _batch(**one), cos=0) == -1
     assert _decode(lib, _batch(**one), max_pos=0) == -1
+    assert _decode(lib, _batch(**one), max_pos=1 << 22) == -1
     assert _decode(lib, _batch(**one), ws=16) == -3
     assert _decode(lib, _batch(**one, head_dim=96)) == -2
     # the pre-rotated variant needs no table; an empty batch is a no-op
