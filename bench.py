@@ -269,6 +269,18 @@ def graph_steps(step, ms_step, reps=5):
             "ms_per_step_all": [round(t, 5) for t in times]}
 
 
+def shader_clock_mhz(workspace):
+    """Shader clock over the attention kernel's last launch, from the clock stamps
+    its first work-group leaves at bytes 128..159 of the workspace (shader clock
+    counter and 100 MHz real-time counter at start and end), or None."""
+    import torch
+    torch.cuda.synchronize()
+    c0, r0, c1, r1 = (int(v) for v in workspace[128:160].view(torch.int64).cpu().tolist())
+    if r1 <= r0 or c1 <= c0:
+        return None
+    return round(100.0 * (c1 - c0) / (r1 - r0), 1)
+
+
 def steps_kernel_ms(step, n):
     """Average (plan, attention, merge) kernel durations over n back-to-back calls of `step` (each making one
     attention call), from the HIP events the library records around its launches, read after the last step."""
@@ -517,6 +529,7 @@ def main():
     # steps): the kernels' durations inside the step sequence
     ms_plan, ms_kernel, ms_merge = steps_kernel_ms(dw.step, a.steps)
     ms_attn = ms_plan + ms_kernel + ms_merge
+    sclk = shader_clock_mhz(dw.workspace)
     # the pre-rotated reference kernel in the same sequence (write_kv, then the call)
     def step_prerotated():
         dw.write_new()
@@ -540,7 +553,7 @@ def main():
     ms_wkv = timed(dw.write_new, reps)
     log(f"[bench] kernels in the timed steps: plan {ms_plan:.4f} ms, attention {ms_kernel:.4f} ms, "
         f"merge {ms_merge:.4f} ms; attention without RoPE {ms_kernel_prerot:.4f} ms; write_kv {ms_wkv:.4f} ms; "
-        f"cold caches: attention {ms_kernel_cold:.4f} ms")
+        f"cold caches: attention {ms_kernel_cold:.4f} ms; shader clock {sclk} MHz")
 
     tflops = flops / (ms_kernel * 1e-3) / 1e12
     call_tflops = flops / (ms_attn * 1e-3) / 1e12
@@ -608,6 +621,7 @@ def main():
                            "merge_kernel_ms": round(ms_merge_cold, 5),
                            "tflops_attention_kernel": round(flops / (ms_kernel_cold * 1e-3) / 1e12, 2)},
             "rope_overhead_pct": round(100 * (ms_kernel / ms_kernel_prerot - 1), 2),
+            "shader_clock_mhz": sclk,
             "pct_hbm_peak_attention_kernel": round(100 * algorithmic_bytes(w) / (ms_kernel * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
             "write_kv_ms": round(ms_wkv, 5),
             "write_kv_GBps": round(kv_bytes / (ms_wkv * 1e-3) / 1e9, 1),

@@ -182,6 +182,11 @@ int minipic_get_launch_info(const minipic_batch* batch, int32_t dtype, minipic_l
  *              MINIPIC_EW_* bits when they meet out-of-range metadata (after
  *              clamping it); the caller may read it after its own sync and
  *              should zero it to reset it. The library never reads it back.
+ *              Bytes 128..159 (measurement only) hold four uint64_t stamps of
+ *              the attention kernel's first work-group: the shader clock
+ *              counter and the 100 MHz real-time counter when it starts, then
+ *              both again when it has no work left; the shader clock in MHz is
+ *              100 * (clock difference) / (real-time difference).
  * Query head h reads KV head h / (num_q_heads / num_kv_heads).
  */
 int minipic_prefill_attn(const void* q, const void* k_cache, const void* v_cache, int64_t num_blocks,

@@ -479,6 +479,10 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
   const float sl2 = P.scale_log2;
   const rsrc_t tab = make_rsrc(P.cos_sin, P.max_pos * D * 4);
 
+  if (blockIdx.x == 0 && tid == 0) {   // measurement: clock stamps of work-group 0
+    P.hdr->clk_start = clock64();
+    P.hdr->rt_start = wall_clock64();
+  }
   if (tid < kQueues) {
     s_qs[tid] = P.hdr->qstart[tid];
     s_qc[tid] = P.hdr->qcount[tid];
@@ -860,6 +864,10 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
     }
     it = nxt;
     item = nitem;
+  }
+  if (blockIdx.x == 0 && tid == 0) {
+    P.hdr->clk_end = clock64();
+    P.hdr->rt_end = wall_clock64();
   }
 }
 

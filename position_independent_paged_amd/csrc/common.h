@@ -76,8 +76,14 @@ struct WsHeader {
   uint32_t next[kQueues];       // per-queue scheduler counters (zeroed by plan_items)
   uint32_t qstart[kQueues];     // first item of each queue
   uint32_t qcount[kQueues];     // items in each queue
+  uint32_t pad[4];
+  // Measurement: the attention kernel's work-group 0 stores the shader clock
+  // counter and the 100 MHz real-time counter when it starts and when it has
+  // drained the queues (the ratio of the differences is the shader clock).
+  uint64_t clk_start, rt_start, clk_end, rt_end;
 };
 static_assert(sizeof(WsHeader) <= 256, "workspace header");
+static_assert(offsetof(WsHeader, clk_start) == 128, "clock stamps at byte 128 of the workspace");
 
 // One split (tile, KV head): its pieces occupy slots slot0 .. slot0+nsplit-1.
 struct Group {
