@@ -195,6 +195,34 @@ int minipic_prefill_attn(const void* q, const void* k_cache, const void* v_cache
                          uint32_t flags, int32_t dtype, void* stream);
 
 /*
+ * minipic_prefill_attn without a caller workspace and without any allocation:
+ * for callers that cannot allocate device memory (code under HIP stream
+ * capture, tight serving loops, harnesses that forbid hipMalloc).
+ *   The workspace is the library's own device array of
+ *   MINIPIC_STATIC_WORKSPACE_BYTES bytes (one per GPU, kept until the process
+ *   ends; its address is looked up on the first call on each device). A batch
+ *   whose minipic_workspace_size() exceeds it is rejected with
+ *   MINIPIC_ERR_WORKSPACE before any HIP call. The call allocates nothing
+ *   (no hipMalloc, hipFree or allocating library routine) and records no
+ *   kernel-timing events.
+ *   err_word : NULL, or a 4-byte aligned device uint32_t of the caller's that
+ *              receives the MINIPIC_EW_* bits (the role of the workspace's
+ *              first word in minipic_prefill_attn); the caller zeroes it and
+ *              reads it after its own sync. With NULL the bits are dropped.
+ *   Every other argument, the result and the kernels are those of
+ *   minipic_prefill_attn, bit for bit.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (each call rebuilds what it reads): calls that can overlap on one
+ * GPU (different streams, or host threads without ordering) race and must not
+ * be made; calls in order on one stream are safe.
+ */
+#define MINIPIC_STATIC_WORKSPACE_BYTES (128u * 1024u * 1024u)
+int minipic_prefill_attn_static(const void* q, const void* k_cache, const void* v_cache, int64_t num_blocks,
+                                const minipic_batch* batch, const float* cos_sin, int32_t max_pos,
+                                float softmax_scale, void* out, uint32_t* err_word, uint32_t flags,
+                                int32_t dtype, void* stream);
+
+/*
  * The same kernel without the in-kernel key rotation: k_cache holds keys that
  * are ALREADY rotated (R_pi(j) k~_j), as in the baseline FlashAttention of
  * "MiniPIC ...", §3.2.2. Used to measure the cost of the rotation. cos_sin /

@@ -32,12 +32,13 @@ EXPORTS = [
     "minipic_kernel_times_all",
     "minipic_decode_workspace_size", "minipic_decode_attn", "minipic_decode_prerotated",
     "minipic_describe_blocks", "minipic_block_cache_create", "minipic_block_cache_destroy",
-    "minipic_block_cache_assign", "minipic_slot_mapping",
+    "minipic_block_cache_assign", "minipic_slot_mapping", "minipic_prefill_attn_static",
 ]
 
 
 MINIPIC_ERR_CONTRACT = -5
 MINIPIC_ERR_CACHE_FULL = -6
+MINIPIC_STATIC_WORKSPACE_BYTES = 128 * 1024 * 1024
 
 
 class minipic_markers(ctypes.Structure):
@@ -102,6 +103,8 @@ def load_library(path: str = None):
             i32, vp]
     lib.minipic_prefill_attn.argtypes = attn
     lib.minipic_reference_prerotated.argtypes = attn
+    lib.minipic_prefill_attn_static.argtypes = [vp, vp, vp, i64, ctypes.POINTER(minipic_batch), vp, i32,
+                                                ctypes.c_float, vp, vp, ctypes.c_uint32, i32, vp]
     lib.minipic_decode_workspace_size.argtypes = [ctypes.POINTER(minipic_batch), i32, ctypes.POINTER(sz)]
     lib.minipic_decode_attn.argtypes = attn
     lib.minipic_decode_prerotated.argtypes = [vp, vp, vp, i64, ctypes.POINTER(minipic_batch), ctypes.c_float, vp,
@@ -190,6 +193,14 @@ def minipic_prefill_attn(q, k_cache, v_cache, num_blocks, batch, cos_sin, max_po
                          flags: int = 0, softmax_scale: float = 0.0, stream=None):
     _attn(load_library().minipic_prefill_attn, q, k_cache, v_cache, num_blocks, batch, cos_sin, max_pos, out,
           workspace, flags, softmax_scale, stream)
+
+
+def minipic_prefill_attn_static(q, k_cache, v_cache, num_blocks, batch, cos_sin, max_pos, out, err_word=None, *,
+                                flags: int = 0, softmax_scale: float = 0.0, stream=None):
+    """minipic_prefill_attn on the library's own workspace (no allocation); err_word: None or a device int32/uint32."""
+    _check(load_library().minipic_prefill_attn_static(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), int(num_blocks), ctypes.byref(batch), _ptr(cos_sin), int(max_pos),
+        float(softmax_scale), _ptr(out), _ptr(err_word), int(flags), _dtype_code(q), _stream(stream)))
 
 
 def minipic_reference_prerotated(q, k_cache, v_cache, num_blocks, batch, out, workspace, *, cos_sin=None,

@@ -555,7 +555,7 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
                 // keys past the context hold no token: any row of the table will do
                 int pos = o2 < nvalid ? lpos[kb * kBlock + o2] : 0;
                 if (pos < 0 || pos >= P.max_pos) {
-                  atomicOr(&P.hdr->err, (uint32_t)MINIPIC_EW_POS);
+                  atomicOr(P.err, (uint32_t)MINIPIC_EW_POS);
                   pos = pos < 0 ? 0 : P.max_pos - 1;
                 }
                 pos_s[i * kBlock + o2] = pos;
@@ -639,7 +639,7 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
       } else if (valid) {
         int pos = lpos[rows.c[rb]];
         if (pos < 0 || pos >= P.max_pos) {
-          atomicOr(&P.hdr->err, (uint32_t)MINIPIC_EW_POS);
+          atomicOr(P.err, (uint32_t)MINIPIC_EW_POS);
           pos = pos < 0 ? 0 : P.max_pos - 1;
         }
         const float* cs = P.cos_sin + (int64_t)pos * D;

@@ -71,7 +71,7 @@ __global__ void __launch_bounds__(kNTf) attn_f32_kernel(AttnParams P) {
       if (P.flags & MINIPIC_FLAG_ROTATE_Q) {
         int pos = rvalid ? lpos[c_row] : 0;
         if (pos < 0 || pos >= P.max_pos) {
-          atomicOr(&P.hdr->err, (uint32_t)MINIPIC_EW_POS);
+          atomicOr(P.err, (uint32_t)MINIPIC_EW_POS);
           pos = pos < 0 ? 0 : P.max_pos - 1;
         }
         const float* cs = P.cos_sin + (int64_t)pos * D;
@@ -109,7 +109,7 @@ __global__ void __launch_bounds__(kNTf) attn_f32_kernel(AttnParams P) {
               // a key past the context holds no token (never visible): any table row will do
               int pos = key >= bd.nvalid ? 0 : (bd.pos0 >= 0 ? bd.pos0 + key : lpos[bd.kb * kBlock + key]);
               if (pos < 0 || pos >= P.max_pos) {
-                atomicOr(&P.hdr->err, (uint32_t)MINIPIC_EW_POS);
+                atomicOr(P.err, (uint32_t)MINIPIC_EW_POS);
                 pos = pos < 0 ? 0 : P.max_pos - 1;
               }
               const float c = P.cos_sin[(int64_t)pos * D + i];

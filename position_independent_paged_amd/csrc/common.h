@@ -69,7 +69,7 @@ constexpr int kDecodeMaxSplits = 4096;   // key splits per (request, KV head) in
 
 // Header of the workspace (first 256 bytes).
 struct WsHeader {
-  uint32_t err;                 // MINIPIC_EW_* bits
+  uint32_t err;                 // MINIPIC_EW_* bits of calls that take the workspace from the caller
   uint32_t num_items;           // written by plan_items
   uint32_t chunk;               // key blocks per piece chosen by plan_items
   uint32_t num_groups;          // split (tile, KV head) groups listed for the merge
@@ -156,6 +156,7 @@ struct PlanParams {
   const int32_t* span_id;
   const uint8_t* blk_flags;
   WsHeader* hdr;
+  uint32_t* err;       // MINIPIC_EW_* bits (the workspace's first word, or the caller's word)
   TileDesc* tiles;
   TokDesc* toks;       // [num_tiles][bq]
   BlkDesc* blist;      // [num_tiles][max_blocks]
@@ -185,6 +186,7 @@ struct AttnParams {
   const float* cos_sin;
   const int32_t* logical_pos;
   WsHeader* hdr;
+  uint32_t* err;       // MINIPIC_EW_* bits (the workspace's first word, or the caller's word)
   const TileDesc* tiles;
   const TokDesc* toks;
   const BlkDesc* blist;

@@ -3,7 +3,9 @@
 // HIP call, so a rejected call never touches the GPU.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
+#include <mutex>
 #include <vector>
 #include <cstdarg>
 #include <cstdio>
@@ -31,6 +33,13 @@ hipError_t launch_decode_merge(const DecodeParams& p, int D, int G, hipStream_t 
 }  // namespace minipic
 
 using namespace minipic;
+
+// Workspace of minipic_prefill_attn_static: device memory the library owns,
+// one copy on every GPU that runs that entry point, held until the process
+// ends. On the host this name stands for a host-side stand-in, not a device
+// address; host code takes each device's address from hipGetSymbolAddress
+// (static_workspace below) and never uses the name itself.
+static __device__ __align__(256) unsigned char scratch[MINIPIC_STATIC_WORKSPACE_BYTES];
 
 namespace {
 
@@ -233,6 +242,34 @@ int run_decode(const void* q, const void* k_cache, const void* v_cache, int64_t 
   return MINIPIC_OK;
 }
 
+// Device address of `scratch` on the current device: hipGetSymbolAddress on
+// the first call on each device (with that device current, return code
+// checked), the kept address after that.
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+int static_workspace(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MINIPIC_ERR_UNSUPPORTED, "device %d: the static workspace serves devices 0..%d", dev, kMaxDevices - 1);
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+      if (!p || (uintptr_t)p % kAlign) return fail(MINIPIC_ERR_HIP, "static workspace at %p is not 256-byte aligned", p);
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return MINIPIC_OK;
+}
+
 int env_int(const char* name, int dflt) {
   const char* s = std::getenv(name);
   if (!s || !*s) return dflt;
@@ -309,7 +346,7 @@ int persistent_grid(int dtype, int D, int G, bool rope, int* grid) {
 int run_attention(const void* q, const void* k_cache, const void* v_cache, int64_t num_blocks,
                   const minipic_batch* b, const float* cos_sin, int32_t max_pos, float softmax_scale,
                   void* out, void* workspace, size_t workspace_bytes, uint32_t flags, int32_t dtype,
-                  void* stream, bool rope) {
+                  void* stream, bool rope, bool static_ws = false, uint32_t* err_word = nullptr) {
   int st = check_batch(b, dtype);
   if (st) return st;
   if (flags & ~(uint32_t)MINIPIC_FLAG_ROTATE_Q) return fail(MINIPIC_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
@@ -327,12 +364,23 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, int64
     return fail(MINIPIC_ERR_INVALID_ARG, "softmax_scale is not finite");
   Plan pl;
   make_plan(b, dtype, &pl);
-  if (!workspace) return fail(MINIPIC_ERR_INVALID_ARG, "workspace is NULL");
-  if ((uintptr_t)workspace % kAlign) return fail(MINIPIC_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
-  if (workspace_bytes < pl.bytes)
-    return fail(MINIPIC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, pl.bytes);
+  if (static_ws) {
+    if ((uintptr_t)err_word % alignof(uint32_t)) return fail(MINIPIC_ERR_INVALID_ARG, "err_word must be 4-byte aligned");
+    if (pl.bytes > (size_t)MINIPIC_STATIC_WORKSPACE_BYTES)
+      return fail(MINIPIC_ERR_WORKSPACE, "batch needs %zu bytes of workspace; the static workspace holds %zu",
+                  pl.bytes, (size_t)MINIPIC_STATIC_WORKSPACE_BYTES);
+  } else {
+    if (!workspace) return fail(MINIPIC_ERR_INVALID_ARG, "workspace is NULL");
+    if ((uintptr_t)workspace % kAlign) return fail(MINIPIC_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    if (workspace_bytes < pl.bytes)
+      return fail(MINIPIC_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, pl.bytes);
+  }
   if (pl.tiles > (int64_t)INT32_MAX / 2 || pl.max_items > (int64_t)INT32_MAX / 2)
     return fail(MINIPIC_ERR_INVALID_ARG, "batch too large for one launch");
+  if (static_ws) {
+    st = static_workspace(&workspace);
+    if (st) return st;
+  }
   const int G = b->num_q_heads / b->num_kv_heads;
   int grid = 0;
   if (persistent_grid(dtype, b->head_dim, G, rope, &grid) != 0)
@@ -347,6 +395,9 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, int64
   Q.span_id = b->span_id;
   Q.blk_flags = b->blk_flags;
   Q.hdr = (WsHeader*)ws;
+  // the static workspace is shared by every call on the GPU: its error bits
+  // go to the caller's word (or, without one, to a header word nobody reads)
+  Q.err = static_ws && err_word ? err_word : &Q.hdr->err;
   Q.tiles = (TileDesc*)(ws + pl.off_tiles);
   Q.toks = (TokDesc*)(ws + pl.off_toks);
   Q.blist = (BlkDesc*)(ws + pl.off_blist);
@@ -374,6 +425,7 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, int64
   P.cos_sin = cos_sin;
   P.logical_pos = b->logical_pos;
   P.hdr = Q.hdr;
+  P.err = Q.err;
   P.tiles = Q.tiles;
   P.toks = Q.toks;
   P.blist = Q.blist;
@@ -390,20 +442,23 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, int64
   P.scale_log2 = scale * 1.4426950408889634f;
   P.flags = flags;
   hipStream_t s = (hipStream_t)stream;
-  g_timer.valid = false;
-  hipError_t e = timer_mark(0, s);
+  // calls on the static workspace record no timing events (creating them allocates)
+  const bool timed = !static_ws;
+  auto mark = [&](int i) { return timed ? timer_mark(i, s) : hipSuccess; };
+  if (timed) g_timer.valid = false;
+  hipError_t e = mark(0);
   if (e == hipSuccess) e = launch_plan(Q, pl.bq, s);
   if (e != hipSuccess) return hip_fail(e, "plan launch");
-  e = timer_mark(1, s);
+  e = mark(1);
   if (e == hipSuccess)
     e = dtype == MINIPIC_BF16 ? launch_attn_bf16(P, b->head_dim, G, rope, grid, s)
                               : launch_attn_f32(P, b->head_dim, G, rope, grid, s);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
-  e = timer_mark(2, s);
+  e = mark(2);
   if (e == hipSuccess) e = launch_merge(P, b->head_dim, dtype, pl.rows, G, pl.max_groups, s);
-  if (e == hipSuccess) e = timer_mark(3, s);
+  if (e == hipSuccess) e = mark(3);
   if (e != hipSuccess) return hip_fail(e, "merge launch");
-  g_timer.valid = g_timer.on;
+  if (timed) g_timer.valid = g_timer.on;
   return MINIPIC_OK;
 }
 
@@ -499,6 +554,14 @@ int minipic_prefill_attn(const void* q, const void* k_cache, const void* v_cache
                          void* stream) {
   return run_attention(q, k_cache, v_cache, num_blocks, batch, cos_sin, max_pos, softmax_scale, out, workspace,
                        workspace_bytes, flags, dtype, stream, /*rope=*/true);
+}
+
+int minipic_prefill_attn_static(const void* q, const void* k_cache, const void* v_cache, int64_t num_blocks,
+                                const minipic_batch* batch, const float* cos_sin, int32_t max_pos,
+                                float softmax_scale, void* out, uint32_t* err_word, uint32_t flags, int32_t dtype,
+                                void* stream) {
+  return run_attention(q, k_cache, v_cache, num_blocks, batch, cos_sin, max_pos, softmax_scale, out, nullptr, 0,
+                       flags, dtype, stream, /*rope=*/true, /*static_ws=*/true, err_word);
 }
 
 int minipic_reference_prerotated(const void* q, const void* k_cache, const void* v_cache, int64_t num_blocks,

@@ -26,7 +26,7 @@ namespace minipic {
 __device__ __forceinline__ BlkDesc blk_from(const PlanParams& P, int ph, const int4 (&pp)[kBlock / 4], int L, int kb,
                                             int span, int flags, int full) {
   if (ph < 0 || (int64_t)ph >= P.num_blocks) {
-    atomicOr(&P.hdr->err, (uint32_t)MINIPIC_EW_BLOCK);
+    atomicOr(P.err, (uint32_t)MINIPIC_EW_BLOCK);
     ph = -1;  // read as zeros by the attention kernels
   }
   int p[kBlock];
@@ -101,7 +101,7 @@ __global__ void __launch_bounds__(NT) plan_tiles_kernel(PlanParams P) {
   int L = P.ctx_len[r];
   const int Lmax = P.max_blocks * kBlock;
   if (L > Lmax || L < 0) {
-    if (tid == 0) atomicOr(&P.hdr->err, (uint32_t)MINIPIC_EW_CTX);
+    if (tid == 0) atomicOr(P.err, (uint32_t)MINIPIC_EW_CTX);
     L = L < 0 ? 0 : Lmax;
   }
   const int cq = tid < nq ? P.q_ctx_idx[row0 + tid] : 0;
@@ -123,7 +123,7 @@ __global__ void __launch_bounds__(NT) plan_tiles_kernel(PlanParams P) {
   if (valid) {
     c = cq;
     if (c < 0 || c >= L) {
-      atomicOr(&P.hdr->err, (uint32_t)MINIPIC_EW_QCTX);
+      atomicOr(P.err, (uint32_t)MINIPIC_EW_QCTX);
       c = c < 0 ? 0 : L - 1;
       if (c < 0) valid = false;  // empty context: the row has nothing to attend
     }
@@ -269,7 +269,7 @@ __global__ void __launch_bounds__(NT) plan_tiles_kernel(PlanParams P) {
       }
     n += tot;
   }
-  if (broken) atomicOr(&P.hdr->err, (uint32_t)MINIPIC_EW_SPAN);
+  if (broken) atomicOr(P.err, (uint32_t)MINIPIC_EW_SPAN);
   if (tid == 0) *td = TileDesc{r, row0, nq, n, 0, -1, 0, 0};
 }
 

@@ -181,6 +181,36 @@ def test_launch_plan_and_workspace():
     assert pip.minipic_workspace_size(small, 0) < 8 << 20
 
 
+def test_static_entry_rejects_on_the_host():
+    """The allocation-free entry point refuses, before any HIP call, a batch whose workspace exceeds its array."""
+    lib = pip.load_library()
+    cap = pip.MINIPIC_STATIC_WORKSPACE_BYTES
+
+    def call(b, err_word=None):
+        return lib.minipic_prefill_attn_static(256, 256, 256, 10, ctypes.byref(b), 256, 1024, 0.0, 256, err_word, 0,
+                                               pip.MINIPIC_BF16, None)
+    big = _batch(total_q=65536, max_q_len=65536, max_ctx_len=131072, max_blocks_per_req=8192)
+    assert pip.minipic_workspace_size(big, pip.MINIPIC_BF16) > cap
+    assert call(big) == -3
+    msg = lib.minipic_last_error()
+    assert b"static workspace holds" in msg and str(cap).encode() in msg
+    # every workload of the benchmark fits
+    for name in ("c1", "c2", "c3", "c3w", "c4", "c5", "e4"):
+        w = workload.make_config(name)
+        assert metrics_workspace_bytes(w) <= cap, name
+    assert call(_batch(), err_word=258) == -1          # err_word not 4-byte aligned
+    assert call(_batch(num_kv_heads=3)) == -2         # the usual batch checks apply
+    assert call(_batch(num_reqs=0)) == 0                          # nothing to do: no HIP call
+
+
+def metrics_workspace_bytes(w):
+    qi = np.asarray(w.q_indptr)
+    b = _batch(num_reqs=w.num_reqs, num_q_heads=w.num_q_heads, num_kv_heads=w.num_kv_heads, head_dim=w.head_dim,
+               max_blocks_per_req=w.block_table.shape[1], total_q=int(qi[-1]), max_q_len=int(np.diff(qi).max()),
+               max_ctx_len=int(w.ctx_len.max()))
+    return pip.minipic_workspace_size(b, pip.MINIPIC_BF16 if w.dtype == "bf16" else pip.MINIPIC_F32)
+
+
 @pytest.mark.parametrize("name", ["c1", "c1_cached", "c3_small", "c4_small", "c5_small", "c2"])
 def test_pair_counter_matches_oracle_mask(name):
     w = workload.make_config(name)
