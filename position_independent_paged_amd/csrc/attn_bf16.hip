@@ -10,9 +10,15 @@
 // head, piece of the tile's visible-block list) from the per-XCD queues.
 //
 // One work item = 256 query rows = BQ query tokens x G query heads sharing
-// KV head g (G = Hq/Hkv). A work-group has NW waves (a build parameter, 8 by
-// default); wave w owns RB blocks of 32 rows (rows 32 RB w + 32 rb + (l % 32));
-// every K or V fragment read from LDS feeds RB MFMAs.
+// KV head g (G = Hq/Hkv). A work-group has 12 waves in two roles, three per
+// SIMD at 168 VGPRs each (waves w, w + 4 and w + 8 share a SIMD):
+//   * 8 consumer waves, 32 query rows each (rows 32 w + (l % 32)): QK^T, the
+//     online softmax and PV on MFMA;
+//   * 4 producer waves: the global loads of the K tiles, their cos/sin rows
+//     and the V tiles, the rotation of K, and the stores of both to LDS.
+// Splitting the roles keeps the staging registers out of the consumers,
+// which is what lets three waves share a SIMD (and two consumers
+// alternate between MFMA and vector work while the producer streams).
 //   * a pipeline step covers 32 keys = 2 cache blocks of the list.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: keys on the M side, queries on
 //     the N side, so lane l holds 16 keys of ONE query and the row max / sum
@@ -22,18 +28,21 @@
 //     consecutive elements then are the bf16x8 B operand of O^T += V^T P^T.
 //   * V is cached transposed inside each block ([d][16]): the V^T A operand
 //     is one 16-byte LDS read of 8 consecutive keys.
+//   * The K and V fragments of a step are read from LDS through a small ring
+//     that runs ahead of the MFMAs, in an order pinned by scheduling fences,
+//     so an MFMA seldom waits for its operand.
 //   * q is scaled by scale * log2(e) when it is loaded and the QK MFMA chain
 //     starts from minus the running max, so the scores leave the MFMA in log2
 //     units already shifted: P = exp2(S) needs no multiply-add per score.
-//   * Software pipeline with one barrier per step: step s computes
-//     S(s+1) = K(s+1) Q^T and O += V(s) P(s) on MFMA, the softmax of the next
-//     scores, rotates and stores K(s+2) and stores V(s+1) (loaded two steps
-//     before), and issues the loads of K(s+4), cos/sin(s+4) and V(s+3). The
-//     two waves that share a SIMD take these parts in opposite order, so one
-//     issues MFMAs while the other runs vector work. The rotation
-//     (rotate-half, i <-> i + d/2) happens once per work item and tile,
-//     between the global load and the LDS store, in fp32 with one rounding to
-//     bf16.
+//   * Software pipeline with one barrier per step: in step s the consumers
+//     compute S(s+1) = K(s+1) Q^T and O += V(s) P(s) and the softmax of the
+//     next scores, while the producers rotate and store K(s+2), store V(s+1)
+//     (loaded two steps before) and issue the loads of K(s+4), cos/sin(s+4)
+//     and V(s+3). The two consumers that share a SIMD take their parts in
+//     opposite order, so one issues MFMAs while the other runs vector work.
+//     The rotation (rotate-half, i <-> i + d/2) happens once per work item
+//     and tile, between the global load and the LDS store, in fp32 with one
+//     rounding to bf16.
 //   * Global loads are buffer loads: a wave's keys always lie in one cache
 //     block, so the block's base address is a scalar and an invalid block
 //     becomes a zero-size buffer whose loads return zeros.
@@ -86,25 +95,23 @@ __device__ __forceinline__ float xor32_sum(float x) {
 // threads; each thread stages one K unit of CW rotate-half pairs (a key's
 // elements [CW c, CW c + CW) and [d/2 + CW c, d/2 + CW c + CW)) and VU 16-byte
 // V pieces per step.
-#ifndef MINIPIC_RB
-#define MINIPIC_RB 1
-#endif
-#ifndef MINIPIC_NW
-#define MINIPIC_NW (MINIPIC_RB == 1 ? 8 : 4)
-#endif
-constexpr int kRB = MINIPIC_RB;   // row blocks per wave of the built kernels
-constexpr int kNW = MINIPIC_NW;   // waves per work-group of the built kernels
+constexpr int kRB = 1;    // row blocks per consumer wave
+constexpr int kNC = 8;    // consumer waves: QK, softmax, PV of 32 query rows each
+constexpr int kNP = 4;    // producer waves: K/V loads, rotation, LDS stores
+constexpr int kNW = kNC + kNP;
 
 template <int D, int RB>
 struct Cfg {
   static constexpr int NT = 64 * kNW;
-  static constexpr int ROWS = 32 * RB * kNW;     // query rows per work item
-  static constexpr int CW = 4 * D <= NT ? 4 : 8;
+  static constexpr int PT = 64 * kNP;            // producer threads
+  static constexpr int ROWS = 32 * RB * kNC;     // query rows per work item
+  static constexpr int CW = 4 * D <= PT ? 4 : 8;
   static constexpr int KCH = (D / 2) / CW;       // K units per key
   static constexpr int KUNITS = kKT * KCH;
-  static_assert(KUNITS <= NT, "one K unit per thread");
+  static_assert(KUNITS == PT, "one K unit per producer thread");
   static constexpr int VUNITS = 2 * D * 2;       // 2 blocks x D rows x 2 halves of 8 keys
-  static constexpr int VU = (VUNITS + NT - 1) / NT;
+  static constexpr int VU = VUNITS / PT;
+  static_assert(VU * PT == VUNITS, "whole V pieces per producer thread");
   static constexpr int KSTR = D + 8;             // bf16 per K row (16-byte pad: conflict-free MFMA reads)
   static constexpr int VSTR = kKT + 8;           // bf16 per V^T row
   static constexpr int KSZ = kKT * KSTR;
@@ -158,20 +165,18 @@ struct Pre {
 };
 
 template <int D, int RB, bool ROPE>
-__device__ __forceinline__ void prefetch(const StepCtx<D, RB>& cx, int jk, int jv, Pre<D, RB>& pr) {
+__device__ __forceinline__ void prefetch(const StepCtx<D, RB>& cx, int jk, int jv, Pre<D, RB>& pr, int tid) {
   using C = Cfg<D, RB>;
-  const int tid = threadIdx.x;
   const int t0 = __builtin_amdgcn_readfirstlane(tid);
   const int ek = __builtin_amdgcn_readfirstlane(2 * jk + t0 / (C::KCH * kBlock));
   pr.ph_k = cx.lst[ek].phys;
   if (ROPE) pr.pos = cx.pos_s[ek * kBlock + (tid / C::KCH) % kBlock];
 #pragma unroll
   for (int u = 0; u < C::VU; ++u) {
-    const int u0 = __builtin_amdgcn_readfirstlane(tid + u * C::NT);
-    const bool act = (C::VU * C::NT == C::VUNITS) || u0 < C::VUNITS;
+    const int u0 = __builtin_amdgcn_readfirstlane(tid + u * C::PT);
     const int ev = __builtin_amdgcn_readfirstlane(2 * jv + u0 / (2 * D));
-    pr.ph_v[u] = act ? cx.lst[ev].phys : -1;
-    pr.nv_v[u] = act ? cx.lst[ev].nvalid : kBlock;
+    pr.ph_v[u] = cx.lst[ev].phys;
+    pr.nv_v[u] = cx.lst[ev].nvalid;
   }
 }
 
@@ -179,17 +184,15 @@ __device__ __forceinline__ void prefetch(const StepCtx<D, RB>& cx, int jk, int j
 // pr). Past the list or for an invalid block the buffer is empty and the
 // loads return zeros.
 template <int D, int RB, bool ROPE>
-__device__ __forceinline__ void load_k(const StepCtx<D, RB>& cx, const Pre<D, RB>& pr, Stage<D, RB>& st) {
+__device__ __forceinline__ void load_k(const StepCtx<D, RB>& cx, const Pre<D, RB>& pr, Stage<D, RB>& st, int tid) {
   using C = Cfg<D, RB>;
   constexpr int CW = C::CW;
-  const int tid = threadIdx.x;
   const int key = tid / C::KCH, ch = tid % C::KCH;
   // a wave's K units lie in one block and are all active or all idle: derive
   // both from the wave's first thread so the buffer descriptor is scalar
-  const int t0 = __builtin_amdgcn_readfirstlane(tid);
   const int off = key % kBlock;
   const int ph = __builtin_amdgcn_readfirstlane(pr.ph_k);
-  const int bytes = (ph >= 0 && t0 < C::KUNITS) ? kBlock * D * 2 : 0;
+  const int bytes = ph >= 0 ? kBlock * D * 2 : 0;
   const rsrc_t r = make_rsrc(cx.kc + (int64_t)(ph < 0 ? 0 : ph) * cx.group, bytes);
   const int row_b = (off * D + CW * ch) * 2;
   if constexpr (CW == 8) {
@@ -217,11 +220,11 @@ __device__ __forceinline__ void load_k(const StepCtx<D, RB>& cx, const Pre<D, RB
 }
 
 template <int D, int RB>
-__device__ __forceinline__ void load_v(const StepCtx<D, RB>& cx, const Pre<D, RB>& pr, Stage<D, RB>& st) {
+__device__ __forceinline__ void load_v(const StepCtx<D, RB>& cx, const Pre<D, RB>& pr, Stage<D, RB>& st, int tid) {
   using C = Cfg<D, RB>;
 #pragma unroll
   for (int u = 0; u < C::VU; ++u) {
-    const int unit = threadIdx.x + u * C::NT;   // a wave's pieces share one block
+    const int unit = tid + u * C::PT;   // a wave's pieces share one block
     const int rem = unit % (2 * D);
     const int ph = __builtin_amdgcn_readfirstlane(pr.ph_v[u]);
     const rsrc_t r = make_rsrc(cx.vc + (int64_t)(ph < 0 ? 0 : ph) * cx.group, ph >= 0 ? kBlock * D * 2 : 0);
@@ -234,11 +237,9 @@ __device__ __forceinline__ void load_v(const StepCtx<D, RB>& cx, const Pre<D, RB
 // Rotate the staged K unit (rotate-half in fp32, one rounding to bf16) and
 // store it to LDS buffer `buf` in the permuted row order.
 template <int D, int RB, bool ROPE>
-__device__ __forceinline__ void store_k(const StepCtx<D, RB>& cx, int buf, const Stage<D, RB>& st) {
+__device__ __forceinline__ void store_k(const StepCtx<D, RB>& cx, int buf, const Stage<D, RB>& st, int tid) {
   using C = Cfg<D, RB>;
   constexpr int CW = C::CW;
-  const int tid = threadIdx.x;
-  if (C::KUNITS < C::NT && tid >= C::KUNITS) return;
   const int key = tid / C::KCH, ch = tid % C::KCH;
   uint32_t ra[CW / 2], rb[CW / 2];
 #pragma unroll
@@ -266,12 +267,11 @@ __device__ __forceinline__ void store_k(const StepCtx<D, RB>& cx, int buf, const
 }
 
 template <int D, int RB>
-__device__ __forceinline__ void store_v(const StepCtx<D, RB>& cx, int buf, const Stage<D, RB>& st) {
+__device__ __forceinline__ void store_v(const StepCtx<D, RB>& cx, int buf, const Stage<D, RB>& st, int tid) {
   using C = Cfg<D, RB>;
 #pragma unroll
   for (int u = 0; u < C::VU; ++u) {
-    const int unit = threadIdx.x + u * C::NT;
-    if (C::VUNITS % C::NT != 0 && unit >= C::VUNITS) continue;
+    const int unit = tid + u * C::PT;
     const int bk = unit / (2 * D);
     const int rem = unit % (2 * D);
     u32x4 val = st.v[u];
@@ -294,12 +294,14 @@ __device__ __forceinline__ void store_v(const StepCtx<D, RB>& cx, int buf, const
 // max of the lane's query row), so the scores leave the MFMA already shifted.
 template <int D, int RB>
 __device__ __forceinline__ void qk(const StepCtx<D, RB>& cx, int buf, const bf16x8 (&qf)[RB][D / 16],
-                                   const f32x16 (&bias)[RB], f32x16 (&s)[RB]) {
+                                   const float (&bias)[RB], f32x16 (&s)[RB]) {
   using C = Cfg<D, RB>;
   const int lane = threadIdx.x & 63;
   const __bf16* kb_ = cx.kl + buf * C::KSZ + (lane & 31) * C::KSTR + 8 * (lane >> 5);
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) s[rb] = bias[rb];
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[rb][i] = bias[rb];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
     const bf16x8 a = *(const bf16x8*)(kb_ + 16 * ks);
@@ -308,21 +310,39 @@ __device__ __forceinline__ void qk(const StepCtx<D, RB>& cx, int buf, const bf16
   }
 }
 
-// O^T += V^T P^T for the 32 keys in V buffer `buf`, all row blocks of the wave.
+// S(s+1) = K Q^T from K buffer kbuf and O += V P from V buffer vbuf (one row
+// block per wave): the LDS fragment reads run kRing ahead of the MFMAs in a
+// ring (program order pinned with scheduling fences), so an MFMA seldom waits
+// on an LDS read.
+constexpr int kRing = 2;
 template <int D, int RB>
-__device__ __forceinline__ void pv(const StepCtx<D, RB>& cx, int buf, const bf16x8 (&pk)[RB][2],
-                                   f32x16 (&o)[RB][D / 32]) {
+__device__ __forceinline__ void qk_pv(const StepCtx<D, RB>& cx, int kbuf, int vbuf, const bf16x8 (&qf)[RB][D / 16],
+                                      const float (&bias)[RB], f32x16 (&s)[RB], const bf16x8 (&pk)[RB][2],
+                                      f32x16 (&o)[RB][D / 32]) {
   using C = Cfg<D, RB>;
+  static_assert(RB == 1, "one row block per wave");
   const int lane = threadIdx.x & 63;
-  const __bf16* vb_ = cx.vl + buf * C::VSZ + (lane & 31) * C::VSTR + 8 * (lane >> 5);
+  const __bf16* kb_ = cx.kl + kbuf * C::KSZ + (lane & 31) * C::KSTR + 8 * (lane >> 5);
+  const __bf16* vb_ = cx.vl + vbuf * C::VSZ + (lane & 31) * C::VSTR + 8 * (lane >> 5);
+  constexpr int NK = D / 16, NV = 2 * (D / 32), N = NK + NV;
+  auto addr = [&](int i) -> const bf16x8* {
+    return i < NK ? (const bf16x8*)(kb_ + 16 * i)
+                  : (const bf16x8*)(vb_ + 32 * ((i - NK) / 2) * C::VSTR + 16 * ((i - NK) % 2));
+  };
+  bf16x8 ring[kRing];
 #pragma unroll
-  for (int dg = 0; dg < D / 32; ++dg)
+  for (int i = 0; i < kRing; ++i) ring[i] = *addr(i);
 #pragma unroll
-    for (int sh = 0; sh < 2; ++sh) {
-      const bf16x8 a = *(const bf16x8*)(vb_ + 32 * dg * C::VSTR + 16 * sh);
+  for (int i = 0; i < 16; ++i) s[0][i] = bias[0];
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) o[rb][dg] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[rb][sh], o[rb][dg], 0, 0, 0);
-    }
+  for (int i = 0; i < N; ++i) {
+    const bf16x8 a = ring[i % kRing];
+    if (i < NK) s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[0][i], s[0], 0, 0, 0);
+    else o[0][(i - NK) / 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[0][(i - NK) % 2], o[0][(i - NK) / 2], 0, 0, 0);
+    if (i + kRing < N) ring[i % kRing] = *addr(i + kRing);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 // Bit j: every row of the tile sees every key of step j. One bit per step of
@@ -396,7 +416,7 @@ template <int RB>
 struct MaxState {
   float m[RB];        // running max in log2 units (-inf: no visible key yet)
   float thr[RB];
-  f32x16 bias[RB];    // -m, or 0 while m is -inf (the QK MFMA's C operand)
+  float bias[RB];     // -m, or 0 while m is -inf (every element of the QK MFMA's C operand)
 };
 
 // Shift the rows whose scores crossed the threshold to their new max: the
@@ -417,11 +437,9 @@ __device__ __forceinline__ void raise_max(const float (&mx)[RB], MaxState<RB>& m
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[rb][dg][i] *= alpha;
     lsum[rb] *= alpha;
+    ms.bias[rb] -= delta;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      sc[rb][i] -= delta;
-      ms.bias[rb][i] -= delta;
-    }
+    for (int i = 0; i < 16; ++i) sc[rb][i] -= delta;
     if (up) {
       ms.m[rb] = m_new;
       ms.thr[rb] = 8.0f;
@@ -446,8 +464,15 @@ __device__ __forceinline__ Item load_item(const Item* items, int i) {
   return t;
 }
 
+// Role of a wave, as a type: the two roles run the item loop as separate
+// instances, so that neither keeps the other's registers live.
+template <bool B>
+struct Role {
+  static constexpr bool prod = B;
+};
+
 template <int D, int G, bool ROPE, int RB>
-__global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams P) {
+__global__ void __launch_bounds__(64 * kNW, 1) attn_bf16_kernel(AttnParams P) {
   using C = Cfg<D, RB>;
   using St = Stage<D, RB>;
   constexpr int NT = C::NT;
@@ -471,8 +496,11 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
   const int w = tid >> 6;
   const int l32 = lane & 31;
   const int h = lane >> 5;
-  // waves w and w + 4 share a SIMD; the first four lead (see the step loop)
-  const bool lead = NT < 512 || w < 4;
+  // waves w, w + 4 and w + 8 share a SIMD: consumers w < 4 lead, w + 4
+  // trail (see the step loop), w + 8 produces
+  const bool producer = w >= kNC;
+  const bool lead = w < 4;
+  const int pt = tid - 64 * kNC;   // producer thread index
 
   const __bf16* kc = (const __bf16*)P.k_cache;
   const __bf16* vc = (const __bf16*)P.v_cache;
@@ -491,6 +519,10 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
   __syncthreads();
   if (tid == 0) s_first = resolve_ticket(P.hdr, s_qs, s_qc, q_cur, atomicAdd(&P.hdr->next[q_cur], 1u));
   __syncthreads();
+  // the two roles run the same items and barriers in loops of their own
+  // (so that neither keeps the other's registers live)
+  auto run = [&](auto role) {
+  constexpr bool prod = decltype(role)::prod;
   int it = __builtin_amdgcn_readfirstlane(s_first);
   Item item{};
   if (it >= 0) item = load_item(P.items, it);
@@ -585,6 +617,7 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
     // registers across the item loop)
     int ln = lane;
     asm volatile("" : "+v"(ln));
+    if constexpr (!prod) {
 #pragma unroll
     for (int k0 = 0; k0 < QLD; k0 += QGR) {
       u32x4 qv[QGR];
@@ -615,10 +648,12 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
       rows.lo[rb] = tk.lo;
       rows.pdep[rb] = valid && tk.pdep;
     }
+    }
     // the claim is issued after the list and q loads: loads retire in issue
     // order, so the waits for them do not wait for the atomic as well
     if (tid == 0) ticket = atomicAdd(&P.hdr->next[q_cur], 1u);
     store_list(min(kListMax, item.p1 - item.p0));
+    if constexpr (!prod)
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const bool valid = rows.valid[rb];
@@ -676,7 +711,7 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
     for (int rb = 0; rb < RB; ++rb) {
       mst.m[rb] = -INFINITY;
       mst.thr[rb] = -INFINITY;
-      mst.bias[rb] = f32x16{};
+      mst.bias[rb] = 0.f;
       lsum[rb] = 0.f;
     }
 
@@ -707,21 +742,23 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
       // load has two steps to arrive.
       St sa, sb;
       Pre<D, RB> pr;
-      prefetch<D, RB, ROPE>(cx, 0, 0, pr);
-      load_k<D, RB, ROPE>(cx, pr, sa);
-      load_v<D, RB>(cx, pr, sa);
-      prefetch<D, RB, ROPE>(cx, 1, 1, pr);
-      load_k<D, RB, ROPE>(cx, pr, sb);
-      store_k<D, RB, ROPE>(cx, 0, sa);
-      store_v<D, RB>(cx, 0, sa);
-      prefetch<D, RB, ROPE>(cx, 2, 1, pr);
-      load_k<D, RB, ROPE>(cx, pr, sa);
-      load_v<D, RB>(cx, pr, sa);
-      store_k<D, RB, ROPE>(cx, 1, sb);
-      prefetch<D, RB, ROPE>(cx, 3, 2, pr);
-      load_k<D, RB, ROPE>(cx, pr, sb);
-      load_v<D, RB>(cx, pr, sb);
-      prefetch<D, RB, ROPE>(cx, kLoadAhead, kLoadAhead - 1, pr);   // the loads of step 0
+      if constexpr (prod) {
+        prefetch<D, RB, ROPE>(cx, 0, 0, pr, pt);
+        load_k<D, RB, ROPE>(cx, pr, sa, pt);
+        load_v<D, RB>(cx, pr, sa, pt);
+        prefetch<D, RB, ROPE>(cx, 1, 1, pr, pt);
+        load_k<D, RB, ROPE>(cx, pr, sb, pt);
+        store_k<D, RB, ROPE>(cx, 0, sa, pt);
+        store_v<D, RB>(cx, 0, sa, pt);
+        prefetch<D, RB, ROPE>(cx, 2, 1, pr, pt);
+        load_k<D, RB, ROPE>(cx, pr, sa, pt);
+        load_v<D, RB>(cx, pr, sa, pt);
+        store_k<D, RB, ROPE>(cx, 1, sb, pt);
+        prefetch<D, RB, ROPE>(cx, 3, 2, pr, pt);
+        load_k<D, RB, ROPE>(cx, pr, sb, pt);
+        load_v<D, RB>(cx, pr, sb, pt);
+        prefetch<D, RB, ROPE>(cx, kLoadAhead, kLoadAhead - 1, pr, pt);   // the loads of step 0
+      }
       uint64_t fm[2];
       full_steps(cx, nsteps, fm);
       if (c0 == item.p0 && tid == 0) s_next = ticket < s_qc[q_cur] ? (int)(s_qs[q_cur] + ticket) : kClaimLate;
@@ -747,19 +784,20 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
       // of K(s+4), V(s+3) into the same stage, read the list entries of the
       // next step's loads
       auto tiles = [&](int s, St& st) {
-        store_k<D, RB, ROPE>(cx, s & 1, st);
-        store_v<D, RB>(cx, (s + 1) & 1, st);
-        load_k<D, RB, ROPE>(cx, pr, st);
-        load_v<D, RB>(cx, pr, st);
-        prefetch<D, RB, ROPE>(cx, s + 1 + kLoadAhead, s + kLoadAhead, pr);
+        store_k<D, RB, ROPE>(cx, s & 1, st, pt);
+        store_v<D, RB>(cx, (s + 1) & 1, st, pt);
+        load_k<D, RB, ROPE>(cx, pr, st, pt);
+        load_v<D, RB>(cx, pr, st, pt);
+        prefetch<D, RB, ROPE>(cx, s + 1 + kLoadAhead, s + kLoadAhead, pr, pt);
       };
       // S(s+1) = K(s+1) Q^T and O += V(s) P(s), with the row sums of P(s)
       auto mfma = [&](int s) {
-        qk<D, RB>(cx, (s + 1) & 1, qf, mst.bias, sc);
-        pv<D, RB>(cx, s & 1, pk, o);
+        qk_pv<D, RB>(cx, (s + 1) & 1, s & 1, qf, mst.bias, sc, pk, o);
       };
-      qk<D, RB>(cx, 0, qf, mst.bias, sc);
-      if (lead) softmax_step(0);
+      if constexpr (!prod) {
+        qk<D, RB>(cx, 0, qf, mst.bias, sc);
+        if (lead) softmax_step(0);
+      }
       __syncthreads();   // K(0) read by every wave before step 0 reuses its buffer
       if (c0 == item.p0) {
         nxt = __builtin_amdgcn_readfirstlane(s_next);
@@ -778,33 +816,38 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
       // step s; one barrier ends each step.
       // The stages alternate with the step's parity, so the loop runs two
       // steps per iteration.
-      auto lead_step = [&](int s, St& st) {
-        mfma(s);
-        if (s + 1 < nsteps) softmax_step(s + 1);
-        tiles(s, st);
-        __syncthreads();
-      };
-      auto trail_step = [&](int s, St& st) {
-        softmax_step(s);
-        tiles(s, st);
-        mfma(s);
-        __syncthreads();
-      };
-      if (lead) {
-        for (int s = 0; s < nsteps; s += 2) {
-          lead_step(s, sa);
-          if (s + 1 < nsteps) lead_step(s + 1, sb);
+      // Consumers compute, producers stage the tiles two steps ahead; one
+      // barrier ends each step of every wave.
+      if constexpr (prod) {
+        int s = 0;
+        for (; s + 1 < nsteps; s += 2) {
+          tiles(s, sa);
+          __syncthreads();
+          tiles(s + 1, sb);
+          __syncthreads();
+        }
+        if (s < nsteps) {
+          tiles(s, sa);
+          __syncthreads();
+        }
+      } else if (lead) {
+        for (int s = 0; s < nsteps; ++s) {
+          mfma(s);
+          if (s + 1 < nsteps) softmax_step(s + 1);
+          __syncthreads();
         }
       } else {
-        for (int s = 0; s < nsteps; s += 2) {
-          trail_step(s, sa);
-          if (s + 1 < nsteps) trail_step(s + 1, sb);
+        for (int s = 0; s < nsteps; ++s) {
+          softmax_step(s);
+          mfma(s);
+          __syncthreads();
         }
       }
     }
 
     // ---- epilogue
-    if (ns == 1) {
+    if constexpr (prod) {
+    } else if (ns == 1) {
       // out = O / l in bf16: the wave's rows go to rowbuf, then every store
       // instruction writes RPI whole rows of out (rows past the tile's end
       // or without keys are not written)
@@ -865,6 +908,9 @@ __global__ void __launch_bounds__(64 * kNW, 8 / kNW) attn_bf16_kernel(AttnParams
     it = nxt;
     item = nitem;
   }
+  };
+  if (producer) run(Role<true>{});
+  else run(Role<false>{});
   if (blockIdx.x == 0 && tid == 0) {
     P.hdr->clk_end = clock64();
     P.hdr->rt_end = wall_clock64();
@@ -890,7 +936,7 @@ static hipError_t launch_g(const AttnParams& p, int G, int grid, hipStream_t s) 
 }
 
 // Query rows per work item and threads per work-group of the built kernels.
-int attn_bf16_rows() { return 32 * kRB * kNW; }
+int attn_bf16_rows() { return 32 * kRB * kNC; }
 int attn_bf16_threads() { return 64 * kNW; }
 
 hipError_t launch_attn_bf16(const AttnParams& p, int D, int G, bool rope, int grid, hipStream_t s) {

@@ -168,7 +168,7 @@ def test_launch_plan_and_workspace():
     info = pip.minipic_get_launch_info(b, 1)
     assert info["tokens_per_tile"] == 64 and info["rows_per_tile"] == 256
     assert info["num_q_tiles"] == 248 and info["num_tiles"] == 248
-    assert info["threads"] == 512
+    assert info["threads"] == 768          # 8 consumer + 4 producer waves
     ws = pip.minipic_workspace_size(b, 1)
     # per-tile key-block lists (16 B per block) and the partial-result slots (fp32 O, m, l per row)
     assert ws >= 248 * 1952 * 16 + info["partial_slots"] * 256 * (128 + 2) * 4
