@@ -19,6 +19,11 @@
 //     lazily raised running max; O^T += V^T P^T on v_mfma_f32_16x16x16bf16_1k,
 //     whose B operand layout is the S accumulator's, and whose A operand is an
 //     8-byte read of the [d][16] V block;
+//   * the block table, span ids and flags are read through the scalar cache
+//     (the block index is wave-uniform), and each block's cos/sin rows are
+//     requested before the next block's K/V: the waits for a block's data
+//     never wait for the following block's loads, so one block stays in
+//     flight behind the one being computed;
 //   * every wave writes its (O, m, l) partial (m in log2 units); a merge
 //     kernel combines the splits of a (request, query head) in split order.
 #include "common.h"
@@ -116,21 +121,37 @@ __global__ void __launch_bounds__(64) decode_bf16_kernel(DecodeParams P) {
           sd[8 * t + e] = cs[D / 2 + 32 * t + e];
         }
     }
+    // Block descriptors through the scalar cache: the block index is uniform,
+    // and scalar loads leave the vector memory counter, which paces the K/V
+    // stream, alone.
+    typedef const __attribute__((address_space(4))) int32_t CI;
+    auto span_at = [&](int b) { return ((const CI*)span)[b]; };
+    auto flg_at = [&](int b) {
+      const uintptr_t a = (uintptr_t)(flg + b);
+      return (int)((((const CI*)(a & ~(uintptr_t)3))[0] >> (8 * (a & 3))) & 0xff);
+    };
     // the next block of the split the query sees, or b1
     auto next_visible = [&](int b) {
+      b = __builtin_amdgcn_readfirstlane(b);
+      bool broken = false;
       for (; b < b1; ++b) {
-        const bool glob = (flg[b] & MINIPIC_BLK_GLOBAL) != 0;
-        const bool same = span[b] == span_q;
-        if (!pdep_q && !glob && same && b < lo_q && l == 0 && g == 0) atomicOr(P.err, (uint32_t)MINIPIC_EW_SPAN);
+        const bool glob = (flg_at(b) & MINIPIC_BLK_GLOBAL) != 0;
+        const bool same = span_at(b) == span_q;
+        broken = broken || (!pdep_q && !glob && same && b < lo_q);
         if (pdep_q || glob || (same && b >= lo_q)) break;
       }
+      if (broken && l == 0 && g == 0) atomicOr(P.err, (uint32_t)MINIPIC_EW_SPAN);
       return b;
     };
     // K rows: lane (n, j) = key n of the block, d slices 8 j of every chunk;
     // V^T operand: lane (n, j) = d row 16 mt + n, keys 4 j .. 4 j + 3; the
     // key's logical position. An invalid block reads as zeros.
     auto load_block = [&](int b, bf16x8 (&ka)[NC], s16x4 (&va)[NM], int& pos) {
-      int ph = btab[b];
+      // a key past the context holds no token: its position is not read (the
+      // lane then follows the block's run of positions, or reads row 0). It
+      // is loaded first, so that waiting for it waits for no K/V load.
+      pos = ROPE && b * kBlock + n < L ? lpos[b * kBlock + n] : 0;
+      int ph = ((const CI*)btab)[b];
       if (ph < 0 || (int64_t)ph >= P.num_blocks) {
         if (l == 0) atomicOr(P.err, (uint32_t)MINIPIC_EW_BLOCK);
         ph = -1;
@@ -148,9 +169,6 @@ __global__ void __launch_bounds__(64) decode_bf16_kernel(DecodeParams P) {
 #pragma unroll
         for (int mt = 0; mt < NM; ++mt) va[mt] = s16x4{0, 0, 0, 0};
       }
-      // a key past the context holds no token: its position is not read (the
-      // lane then follows the block's run of positions, or reads row 0)
-      pos = ROPE && b * kBlock + n < L ? lpos[b * kBlock + n] : 0;
     };
     // one block in flight ahead of the one being computed
     bf16x8 ka_n[NC];
@@ -167,11 +185,11 @@ __global__ void __launch_bounds__(64) decode_bf16_kernel(DecodeParams P) {
       for (int mt = 0; mt < NM; ++mt) va[mt] = va_n[mt];
       int pos = pos_n;
       const int bc = b;
-      b = next_visible(b + 1);
-      if (b < b1) load_block(b, ka_n, va_n, pos_n);
+      // the cos/sin rows of this block are requested before the next block's
+      // K/V, so that waiting for them never waits for the next block
+      f32x4 cw[ROPE ? NH : 1][4];
+      bool cons = false;
       if (ROPE) {
-        // rotate-half at the key's logical position: element i (first half)
-        // with element i + D/2, in fp32, one rounding to bf16
         const bool past = bc * kBlock + n >= L;   // lane 0 (key 0) never is
         if (!past && (pos < 0 || pos >= P.max_pos)) {
           atomicOr(P.err, (uint32_t)MINIPIC_EW_POS);
@@ -181,12 +199,24 @@ __global__ void __launch_bounds__(64) decode_bf16_kernel(DecodeParams P) {
         // p0, shared by the block's 16 keys, and add the angle n theta_i;
         // otherwise read each key's own row
         const int p0 = __builtin_amdgcn_readfirstlane(pos);   // lane 0 holds key 0
-        const bool cons = delta_ok && __all(past || pos == p0 + n);
+        cons = delta_ok && __all(past || pos == p0 + n);
         const float* cs = P.cos_sin + (int64_t)(cons ? p0 : pos) * D + 8 * j;
 #pragma unroll
         for (int t = 0; t < NH; ++t) {
-          const f32x4 c0 = *(const f32x4*)(cs + 32 * t), c1 = *(const f32x4*)(cs + 32 * t + 4);
-          const f32x4 s0 = *(const f32x4*)(cs + D / 2 + 32 * t), s1 = *(const f32x4*)(cs + D / 2 + 32 * t + 4);
+          cw[t][0] = *(const f32x4*)(cs + 32 * t);
+          cw[t][1] = *(const f32x4*)(cs + 32 * t + 4);
+          cw[t][2] = *(const f32x4*)(cs + D / 2 + 32 * t);
+          cw[t][3] = *(const f32x4*)(cs + D / 2 + 32 * t + 4);
+        }
+      }
+      b = next_visible(b + 1);
+      if (b < b1) load_block(b, ka_n, va_n, pos_n);
+      if (ROPE) {
+        // rotate-half at the key's logical position: element i (first half)
+        // with element i + D/2, in fp32, one rounding to bf16
+#pragma unroll
+        for (int t = 0; t < NH; ++t) {
+          const f32x4 c0 = cw[t][0], c1 = cw[t][1], s0 = cw[t][2], s1 = cw[t][3];
           float cv[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
           float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
           if (cons) {
@@ -271,19 +301,23 @@ __global__ void __launch_bounds__(64) decode_bf16_kernel(DecodeParams P) {
 
 // Merge of the splits of one (request, query head): O = sum_s 2^(m_s - m*) O_s /
 // sum_s 2^(m_s - m*) l_s, m* = max_s m_s. One 256-thread work-group per
-// (request, query head): the split weights are computed in parallel into LDS;
-// wave w sums splits w, w + 4, ... (several loads in flight), each lane D/64
-// consecutive elements; the four partial sums are added in wave order.
-template <int D>
+// (request, query head, slice of 32 E elements of d): E = D / 32 (whole
+// rows) for batches of many requests, E = 1 where few (request, head) pairs
+// would leave most of the GPU idle. The split weights are computed in
+// parallel into LDS; the eight 32-lane groups sum splits g, g + 8, ... of the
+// slice (E consecutive elements per lane), and the eight partial sums are
+// added in group order.
+template <int D, int E>
 __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeParams P, int G) {
-  constexpr int E = D / 64;
-  constexpr int UNR = 4;
+  constexpr int NDC = D / (32 * E);   // slices of d
   __shared__ float w_s[kDecodeMaxSplits];
   __shared__ float red[256 / 64][2];
-  __shared__ float part[256 / 64 - 1][D];
+  __shared__ float part[8][32 * E];
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
-  const int h = blockIdx.x % P.hq;
-  const int r = blockIdx.x / P.hq;
+  const int grp = tid >> 5, e = tid & 31;
+  const int dc = blockIdx.x % NDC;
+  const int h = (blockIdx.x / NDC) % P.hq;
+  const int r = blockIdx.x / (NDC * P.hq);
   const int g = h / G, n = h % G;
   const int ns = P.nsplit;
   const int64_t base = (int64_t)(r * P.hkv + g) * ns * G + n;   // split s at base + s G
@@ -306,37 +340,35 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeParams P, int G
   if (l == 0) red[w][1] = dloc;
   __syncthreads();
   const float den = (red[0][1] + red[1][1]) + (red[2][1] + red[3][1]);
+  constexpr int UNR = 4;
   float num[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) num[e] = 0.f;
-  const float* po = P.part_o + base * D + E * l;
-  for (int s0 = w; s0 < ns; s0 += 4 * UNR) {
+  for (int i = 0; i < E; ++i) num[i] = 0.f;
+  const float* po = P.part_o + base * D + 32 * E * dc + E * e;
+  for (int s0 = grp; s0 < ns; s0 += 8 * UNR) {
     float v[UNR][E];
 #pragma unroll
     for (int k = 0; k < UNR; ++k) {
-      const int s = s0 + 4 * k;
+      const int s = s0 + 8 * k;
 #pragma unroll
-      for (int e = 0; e < E; ++e) v[k][e] = s < ns ? po[(int64_t)s * G * D + e] : 0.f;
+      for (int i = 0; i < E; ++i) v[k][i] = s < ns ? po[(int64_t)s * G * D + i] : 0.f;
     }
 #pragma unroll
     for (int k = 0; k < UNR; ++k) {
-      const int s = s0 + 4 * k;
+      const int s = s0 + 8 * k;
       const float wt = s < ns ? w_s[s] : 0.f;
 #pragma unroll
-      for (int e = 0; e < E; ++e) num[e] += wt * v[k][e];
+      for (int i = 0; i < E; ++i) num[i] += wt * v[k][i];
     }
   }
-  if (w > 0) {
 #pragma unroll
-    for (int e = 0; e < E; ++e) part[w - 1][E * l + e] = num[e];
-  }
+  for (int i = 0; i < E; ++i) part[grp][E * e + i] = num[i];
   __syncthreads();
-  if (w == 0) {
-    const float inv = 1.f / den;
-    __bf16* op = (__bf16*)P.out + ((int64_t)r * P.hq + h) * D + E * l;
+  for (int x = tid; x < 32 * E; x += 256) {
+    float t = part[0][x];
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      op[e] = (__bf16)((((num[e] + part[0][E * l + e]) + part[1][E * l + e]) + part[2][E * l + e]) * inv);
+    for (int k = 1; k < 8; ++k) t += part[k][x];
+    ((__bf16*)P.out)[((int64_t)r * P.hq + h) * D + 32 * E * dc + x] = (__bf16)(t / den);
   }
 }
 
@@ -361,9 +393,14 @@ hipError_t launch_decode_bf16(const DecodeParams& p, int D, int G, bool rope, hi
 }
 
 hipError_t launch_decode_merge(const DecodeParams& p, int D, int G, hipStream_t s) {
-  const dim3 grid((unsigned)((int64_t)p.num_reqs * p.hq));
-  if (D == 128) hipLaunchKernelGGL((decode_merge_kernel<128>), grid, dim3(256), 0, s, p, G);
-  else if (D == 64) hipLaunchKernelGGL((decode_merge_kernel<64>), grid, dim3(256), 0, s, p, G);
+  // whole rows per work-group once the (request, head) pairs fill the GPU
+  const int64_t heads = (int64_t)p.num_reqs * p.hq;
+  const bool rows = heads >= 256;
+  const dim3 grid((unsigned)(heads * (rows ? 1 : D / 32)));
+  if (D == 128 && rows) hipLaunchKernelGGL((decode_merge_kernel<128, 4>), grid, dim3(256), 0, s, p, G);
+  else if (D == 128) hipLaunchKernelGGL((decode_merge_kernel<128, 1>), grid, dim3(256), 0, s, p, G);
+  else if (D == 64 && rows) hipLaunchKernelGGL((decode_merge_kernel<64, 2>), grid, dim3(256), 0, s, p, G);
+  else if (D == 64) hipLaunchKernelGGL((decode_merge_kernel<64, 1>), grid, dim3(256), 0, s, p, G);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
