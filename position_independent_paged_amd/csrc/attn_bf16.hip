@@ -494,8 +494,6 @@ __global__ void __launch_bounds__(64 * kNW, 1) attn_bf16_kernel(AttnParams P) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
-  const int l32 = lane & 31;
-  const int h = lane >> 5;
   // waves w, w + 4 and w + 8 share a SIMD: consumers w < 4 lead, w + 4
   // trail (see the step loop), w + 8 produces
   const bool producer = w >= kNC;
@@ -597,61 +595,64 @@ __global__ void __launch_bounds__(64 * kNW, 1) attn_bf16_kernel(AttnParams P) {
         }
       }
     };
+    // The claim goes out first: its answer is needed only at the prologue's
+    // second barrier. The list and q loads behind it retire after it (loads
+    // retire in issue order), which costs little: an atomic at L2 usually
+    // returns before loads that go to HBM.
+    if (tid == 0) ticket = atomicAdd(&P.hdr->next[q_cur], 1u);
     fetch_list(item.p0, min(kListMax, item.p1 - item.p0));
 
     // ---- the lane's query rows
     RowInfo<RB> rows;
-    int row[RB];
     bf16x8 qf[RB][NKS];
     // q rows of the wave: lane i loads 16-byte piece i % CPR of row i / CPR
     // (+ RPI per round), so a load instruction reads RPI whole rows; they go
     // to the wave's rows of rowbuf. A row past the tile's end is read from
     // its last token (an address inside q) and zeroed below, so the loads do
-    // not wait for the row descriptors.
+    // not wait for the row descriptors. All of the wave's q loads and its
+    // rows' descriptors are in flight together (one round trip).
     constexpr int CPR = D / 8;          // 16-byte pieces per row
     constexpr int RPI = 64 / CPR;       // rows per load instruction
     constexpr int QLD = 32 * RB / RPI;  // load instructions per lane
-    constexpr int QGR = QLD < 4 ? QLD : 4;  // of them in flight together
-    // (the lane index is made opaque here so that the row addresses, the
-    // same for every item, are computed when used instead of being kept in
-    // registers across the item loop)
+    // (the lane index is made opaque here so that the row and buffer
+    // addresses derived from it, the same for every item, are computed when
+    // used instead of being kept across the item loop, where they would
+    // not fit in the registers and would go to scratch)
     int ln = lane;
     asm volatile("" : "+v"(ln));
+    const int l32 = ln & 31;
+    const int h = ln >> 5;
     if constexpr (!prod) {
+      u32x4 qv[QLD];
 #pragma unroll
-    for (int k0 = 0; k0 < QLD; k0 += QGR) {
-      u32x4 qv[QGR];
-#pragma unroll
-      for (int k = 0; k < QGR; ++k) {
-        const int rw = 32 * RB * w + RPI * (k0 + k) + ln / CPR;
+      for (int k = 0; k < QLD; ++k) {
+        const int rw = 32 * RB * w + RPI * k + ln / CPR;
         const int tq = rw / G;
         const int tq_in = tq < item.nq ? tq : item.nq - 1;
         qv[k] = *(const u32x4*)((const __bf16*)P.q + (((int64_t)item.row0 + tq_in) * P.hq + g * G + rw % G) * D +
                                 8 * (ln % CPR));
       }
+      TokDesc tk[RB];
 #pragma unroll
-      for (int k = 0; k < QGR; ++k)
-        *(u32x4*)(rowbuf + (32 * RB * w + RPI * (k0 + k) + ln / CPR) * C::KSTR + 8 * (ln % CPR)) = qv[k];
-    }
+      for (int rb = 0; rb < RB; ++rb) tk[rb] = P.toks[(int64_t)item.tile * BQ + (32 * RB * w + 32 * rb + l32) / G];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      row[rb] = 32 * RB * w + 32 * rb + l32;
-      const int tok = row[rb] / G;
+      for (int k = 0; k < QLD; ++k)
+        *(u32x4*)(rowbuf + (32 * RB * w + RPI * k + ln / CPR) * C::KSTR + 8 * (ln % CPR)) = qv[k];
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) qf[rb][ks] = *(const bf16x8*)(rowbuf + row[rb] * C::KSTR + 16 * ks + 8 * h);
-      const TokDesc tk = P.toks[(int64_t)item.tile * BQ + tok];
-      const bool valid = tok < item.nq && tk.c >= 0;
-      rows.valid[rb] = valid;
-      rows.c[rb] = valid ? tk.c : -1;
-      rows.bq[rb] = valid ? (tk.c >> 4) : -1;
-      rows.span[rb] = tk.span;
-      rows.lo[rb] = tk.lo;
-      rows.pdep[rb] = valid && tk.pdep;
+      for (int rb = 0; rb < RB; ++rb) {
+        const int row = 32 * RB * w + 32 * rb + l32;
+        const int tok = row / G;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) qf[rb][ks] = *(const bf16x8*)(rowbuf + row * C::KSTR + 16 * ks + 8 * h);
+        const bool valid = tok < item.nq && tk[rb].c >= 0;
+        rows.valid[rb] = valid;
+        rows.c[rb] = valid ? tk[rb].c : -1;
+        rows.bq[rb] = valid ? (tk[rb].c >> 4) : -1;
+        rows.span[rb] = tk[rb].span;
+        rows.lo[rb] = tk[rb].lo;
+        rows.pdep[rb] = valid && tk[rb].pdep;
+      }
     }
-    }
-    // the claim is issued after the list and q loads: loads retire in issue
-    // order, so the waits for them do not wait for the atomic as well
-    if (tid == 0) ticket = atomicAdd(&P.hdr->next[q_cur], 1u);
     store_list(min(kListMax, item.p1 - item.p0));
     if constexpr (!prod)
 #pragma unroll
@@ -845,7 +846,12 @@ __global__ void __launch_bounds__(64 * kNW, 1) attn_bf16_kernel(AttnParams P) {
       }
     }
 
-    // ---- epilogue
+    // ---- epilogue (the lane's row and buffer addresses are derived again
+    // from an opaque lane index, so none of them stays live across the steps)
+    ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int l32e = ln & 31;
+    const int he = ln >> 5;
     if constexpr (prod) {
     } else if (ns == 1) {
       // out = O / l in bf16: the wave's rows go to rowbuf, then every store
@@ -856,7 +862,7 @@ __global__ void __launch_bounds__(64 * kNW, 1) attn_bf16_kernel(AttnParams P) {
       for (int rb = 0; rb < RB; ++rb) {
         const float inv = 1.f / xor32_sum(lsum[rb]);
         vmask[rb] = (uint32_t)__ballot(rows.valid[rb]);
-        __bf16* rp = rowbuf + row[rb] * C::KSTR + 4 * h;
+        __bf16* rp = rowbuf + (32 * RB * w + 32 * rb + l32e) * C::KSTR + 4 * he;
 #pragma unroll
         for (int dg = 0; dg < NDG; ++dg)
 #pragma unroll
@@ -867,8 +873,6 @@ __global__ void __launch_bounds__(64 * kNW, 1) attn_bf16_kernel(AttnParams P) {
             *(u32x2*)(rp + 32 * dg + 8 * j) = u;
           }
       }
-      int ln = lane;   // opaque: see the q staging
-      asm volatile("" : "+v"(ln));
 #pragma unroll
       for (int k = 0; k < 32 * RB / RPI; ++k) {
         const int rr = RPI * k + ln / CPR;   // row within the wave's rows
@@ -888,7 +892,7 @@ __global__ void __launch_bounds__(64 * kNW, 1) attn_bf16_kernel(AttnParams P) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         const float l_tot = xor32_sum(lsum[rb]);
-        float* po = P.part_o + ((int64_t)slot * C::ROWS + 32 * (RB * w + rb)) * D + 4 * lane;
+        float* po = P.part_o + ((int64_t)slot * C::ROWS + 32 * (RB * w + rb)) * D + 4 * ln;
 #pragma unroll
         for (int dg = 0; dg < NDG; ++dg)
 #pragma unroll
@@ -896,7 +900,8 @@ __global__ void __launch_bounds__(64 * kNW, 1) attn_bf16_kernel(AttnParams P) {
             const f32x4 u = {o[rb][dg][4 * j], o[rb][dg][4 * j + 1], o[rb][dg][4 * j + 2], o[rb][dg][4 * j + 3]};
             *(f32x4*)(po + (dg * 4 + j) * 256) = u;
           }
-        if (h == 0 && rows.valid[rb]) P.part_ml[(int64_t)slot * C::ROWS + row[rb]] = make_float2(mst.m[rb], l_tot);
+        if (he == 0 && rows.valid[rb])
+          P.part_ml[(int64_t)slot * C::ROWS + 32 * RB * w + 32 * rb + l32e] = make_float2(mst.m[rb], l_tot);
       }
     }
     if (nxt == kClaimLate) {
