@@ -299,6 +299,21 @@ def steps_kernel_ms(step, n):
     return [sum(t[i] for t in times) / n for i in range(3)]
 
 
+def calls_ms(call, n):
+    """Average time of n back-to-back calls on the current stream, one event pair around all of them."""
+    import torch
+    call()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        call()
+    e1.record()
+    e1.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
 def private_copy_prerotated(dw, w, reps):
     """Attention kernel time of the pre-rotated reference when every request owns private copies of
     its blocks (a shared span at different positions needs one rotated copy per position)."""
@@ -350,12 +365,19 @@ def decode_entry(name, reps):
     _, attn, merge = steps_kernel_ms(dw.decode, reps)
     prerot = steps_kernel_ms(dw.decode_prerotated, reps)[1]
     gbs = nbytes / (attn * 1e-3) / 1e9
+    # whole calls (decode kernel + merge) back to back between one pair of events: free of
+    # the few microseconds that events around every launch add to such short kernels
+    call_ms = calls_ms(dw.decode, 10 * reps)
+    call_ms_prerot = calls_ms(dw.decode_prerotated, 10 * reps)
     e = {"workload": f"decode step after {name.replace('d', 'c', 1)}: one query row per request (its last "
                      f"context token)", "requests": int(w.num_reqs), "context_tokens": int(w.ctx_len.sum()),
          "algorithmic_MB": round(nbytes / 1e6, 2), "decode_kernel_ms": round(attn, 5),
          "merge_kernel_ms": round(merge, 5), "GBps_kernel": round(gbs, 1),
          "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2), "prerotated_kernel_ms": round(prerot, 5),
-         "rope_overhead_pct": round(100 * (attn / prerot - 1), 2)}
+         "rope_overhead_pct": round(100 * (attn / prerot - 1), 2),
+         "call_ms_back_to_back": round(call_ms, 5), "prerotated_call_ms_back_to_back": round(call_ms_prerot, 5),
+         "GBps_call_back_to_back": round(nbytes / (call_ms * 1e-3) / 1e9, 1),
+         "rope_overhead_call_pct": round(100 * (call_ms / call_ms_prerot - 1), 2)}
     del dw
     torch.cuda.empty_cache()
     return e
@@ -574,7 +596,8 @@ def main():
         e = suite[name]
         if "decode_kernel_ms" in e:
             log(f"[bench] suite {name}: decode {e['decode_kernel_ms']:.4f} ms, {e['GBps_kernel']:.0f} GB/s, "
-                f"RoPE +{e['rope_overhead_pct']:.1f}%")
+                f"RoPE +{e['rope_overhead_pct']:.1f}%; back-to-back calls {e['call_ms_back_to_back']:.4f} ms "
+                f"(with merge), RoPE +{e['rope_overhead_call_pct']:.1f}%")
         else:
             log(f"[bench] suite {name}: {e['attention_kernel_ms']:.4f} ms, {e['tflops_kernel']:.1f} TFLOP/s, "
                 f"RoPE +{e['rope_overhead_pct']:.1f}%")

@@ -52,9 +52,11 @@ def workload_pairs(w) -> int:
 
 
 def decode_bytes(w) -> int:
-    """Algorithmic HBM bytes of one decode call (one query row per request):
-    q and out rows, K and V of every key block the query sees (once per KV
-    head), and one cos/sin row per visible key position."""
+    """Compulsory HBM bytes of one decode call (one query row per request):
+    q and out rows and K and V of every key the query sees (once per KV head).
+    The cos/sin rows are left out: a block of consecutive positions needs only
+    one table row plus the per-offset angles, so their count depends on the
+    method, not on the problem."""
     elem = 2 if w.dtype == "bf16" else 4
     bs = w.block_size
     total = 2 * int(w.total_q) * w.num_q_heads * w.head_dim * elem
@@ -65,5 +67,5 @@ def decode_bytes(w) -> int:
             fl = np.asarray(w.blk_flags[r][:bq + 1]).astype(np.int64)
             vis = np.ones(bq + 1, bool) if fl[bq] & PDEP else ((fl & GLOBAL) != 0) | (sp == sp[bq])
             keys = int(vis.sum()) * bs - (bs - 1 - int(c) % bs)    # the query's own block up to itself
-            total += keys * (2 * w.num_kv_heads * w.head_dim * elem + w.head_dim * 4)
+            total += keys * 2 * w.num_kv_heads * w.head_dim * elem
     return total
