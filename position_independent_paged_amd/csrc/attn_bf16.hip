@@ -32,8 +32,10 @@
 //     that runs ahead of the MFMAs, in an order pinned by scheduling fences,
 //     so an MFMA seldom waits for its operand.
 //   * q is scaled by scale * log2(e) when it is loaded and the QK MFMA chain
-//     starts from minus the running max, so the scores leave the MFMA in log2
-//     units already shifted: P = exp2(S) needs no multiply-add per score.
+//     starts from minus the running max, laid down by one small MFMA (ones
+//     times -m, with m kept exact in bf16), so the scores leave the MFMA in
+//     log2 units already shifted: P = exp2(S) needs no multiply-add per score,
+//     and no vector instruction copies the shift into the accumulator.
 //   * Software pipeline with one barrier per step: in step s the consumers
 //     compute S(s+1) = K(s+1) Q^T and O += V(s) P(s) and the softmax of the
 //     next scores, while the producers rotate and store K(s+2), store V(s+1)
@@ -117,6 +119,30 @@ struct Cfg {
   static constexpr int KSZ = kKT * KSTR;
   static constexpr int VSZ = D * VSTR;
 };
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// The running-max shift of the scores, made by one small MFMA: with A = (1,
+// 0, 0, 0) in lanes 0..31 (zeros in 32..63) and B = (-m, 0, 0, 0) in lane n
+// (m the running max of query row n, exact in bf16), D[key][n] = -m for every
+// key. The QK chain accumulates on top of it; the broadcast costs no vector
+// instruction per step.
+__device__ __forceinline__ f32x16 bias_mfma(const s16x4& ones, const s16x4& mb) {
+  return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(ones, mb, f32x16{}, 0, 0, 0);
+}
+
+// bf16 operand (-m, 0, 0, 0) for lanes 0..31, zero for lanes 32..63
+__device__ __forceinline__ s16x4 bias_operand(float m, int lane) {
+  const uint32_t b = (m == -INFINITY || lane >= 32) ? 0u : (__float_as_uint(-m) >> 16);
+  return s16x4{(short)b, 0, 0, 0};
+}
+
+// smallest bf16 value >= x (x finite)
+__device__ __forceinline__ float bf16_ceil(float x) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0xffffu) == 0u) return x;
+  return __uint_as_float(x > 0.f ? ((u + 0x10000u) & 0xffff0000u) : (u & 0xffff0000u));
+}
 
 __device__ __forceinline__ int key_perm(int k) {
   // swap bits 2 and 3 (an involution); bits 0, 1, 4 unchanged
@@ -290,18 +316,17 @@ __device__ __forceinline__ void store_v(const StepCtx<D, RB>& cx, int buf, const
 }
 
 // S^T - m for the 32 keys in K buffer `buf`, all row blocks of the wave: the
-// MFMA chain starts from `bias` (every element of a lane is minus the running
-// max of the lane's query row), so the scores leave the MFMA already shifted.
+// MFMA chain starts from the bias MFMA's -m (every element of a lane is minus
+// the running max of the lane's query row), so the scores leave the MFMA
+// already shifted.
 template <int D, int RB>
 __device__ __forceinline__ void qk(const StepCtx<D, RB>& cx, int buf, const bf16x8 (&qf)[RB][D / 16],
-                                   const float (&bias)[RB], f32x16 (&s)[RB]) {
+                                   const s16x4& ones, const s16x4 (&mb)[RB], f32x16 (&s)[RB]) {
   using C = Cfg<D, RB>;
   const int lane = threadIdx.x & 63;
   const __bf16* kb_ = cx.kl + buf * C::KSZ + (lane & 31) * C::KSTR + 8 * (lane >> 5);
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s[rb][i] = bias[rb];
+  for (int rb = 0; rb < RB; ++rb) s[rb] = bias_mfma(ones, mb[rb]);
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
     const bf16x8 a = *(const bf16x8*)(kb_ + 16 * ks);
@@ -317,7 +342,7 @@ __device__ __forceinline__ void qk(const StepCtx<D, RB>& cx, int buf, const bf16
 constexpr int kRing = 2;
 template <int D, int RB>
 __device__ __forceinline__ void qk_pv(const StepCtx<D, RB>& cx, int kbuf, int vbuf, const bf16x8 (&qf)[RB][D / 16],
-                                      const float (&bias)[RB], f32x16 (&s)[RB], const bf16x8 (&pk)[RB][2],
+                                      const s16x4& ones, const s16x4 (&mb)[RB], f32x16 (&s)[RB], const bf16x8 (&pk)[RB][2],
                                       f32x16 (&o)[RB][D / 32]) {
   using C = Cfg<D, RB>;
   static_assert(RB == 1, "one row block per wave");
@@ -332,8 +357,7 @@ __device__ __forceinline__ void qk_pv(const StepCtx<D, RB>& cx, int kbuf, int vb
   bf16x8 ring[kRing];
 #pragma unroll
   for (int i = 0; i < kRing; ++i) ring[i] = *addr(i);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) s[0][i] = bias[0];
+  s[0] = bias_mfma(ones, mb[0]);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < N; ++i) {
@@ -416,33 +440,37 @@ template <int RB>
 struct MaxState {
   float m[RB];        // running max in log2 units (-inf: no visible key yet)
   float thr[RB];
-  float bias[RB];     // -m, or 0 while m is -inf (every element of the QK MFMA's C operand)
+  s16x4 mb[RB];       // B operand of the bias MFMA: -m (exact in bf16), or 0 while m is -inf
 };
 
 // Shift the rows whose scores crossed the threshold to their new max: the
 // scores of this step, the bias of the next ones, O and the row sums.
 template <int D, int RB>
 __device__ __forceinline__ void raise_max(const float (&mx)[RB], MaxState<RB>& ms, f32x16 (&sc)[RB],
-                                          float (&lsum)[RB], f32x16 (&o)[RB][D / 32]) {
+                                          float (&lsum)[RB], f32x16 (&o)[RB][D / 32], int lane) {
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const float rm = xor32_max(mx[rb]);           // shifted row max
     const bool up = rm > ms.thr[rb];
-    const float delta = up ? rm : 0.f;
     const float m_old = ms.m[rb];
-    const float m_new = (m_old == -INFINITY ? 0.f : m_old) + delta;
+    const float base = m_old == -INFINITY ? 0.f : m_old;
+    // the new max is rounded up to a bf16 value (the bias MFMA takes it in
+    // bf16); the shift of this step's scores is the exact difference
+    const float m_new = up ? bf16_ceil(base + rm) : m_old;
+    const float delta = up ? m_new - base : 0.f;
     const float alpha = up ? exp2f(m_old - m_new) : 1.f;   // 0 for a first max (O, l are zero)
 #pragma unroll
     for (int dg = 0; dg < D / 32; ++dg)
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[rb][dg][i] *= alpha;
     lsum[rb] *= alpha;
-    ms.bias[rb] -= delta;
+
 #pragma unroll
     for (int i = 0; i < 16; ++i) sc[rb][i] -= delta;
     if (up) {
       ms.m[rb] = m_new;
       ms.thr[rb] = 8.0f;
+      ms.mb[rb] = bias_operand(m_new, lane);
     }
   }
 }
@@ -515,7 +543,9 @@ __global__ void __launch_bounds__(64 * kNW, 1) attn_bf16_kernel(AttnParams P) {
   }
   int q_cur = blockIdx.x % kQueues;   // queue being drained (thread 0)
   __syncthreads();
-  if (tid == 0) s_first = resolve_ticket(P.hdr, s_qs, s_qc, q_cur, atomicAdd(&P.hdr->next[q_cur], 1u));
+  // the first item is the work-group's own ticket (the planner starts each
+  // queue's counter past the work-groups that drain it)
+  if (tid == 0) s_first = resolve_ticket(P.hdr, s_qs, s_qc, q_cur, blockIdx.x / kQueues);
   __syncthreads();
   // the two roles run the same items and barriers in loops of their own
   // (so that neither keeps the other's registers live)
@@ -707,12 +737,14 @@ __global__ void __launch_bounds__(64 * kNW, 1) attn_bf16_kernel(AttnParams P) {
 #pragma unroll
       for (int i = 0; i < NDG; ++i) o[rb][i] = f32x16{};
     MaxState<RB> mst;
+    // A operand of the bias MFMA: (1, 0, 0, 0) in lanes 0..31
+    const s16x4 ones = (threadIdx.x & 32) ? s16x4{0, 0, 0, 0} : s16x4{(short)0x3f80, 0, 0, 0};
     float lsum[RB];        // the lane's share of the running row sums (lanes l, l ^ 32 add up to row l % 32)
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       mst.m[rb] = -INFINITY;
       mst.thr[rb] = -INFINITY;
-      mst.bias[rb] = 0.f;
+      mst.mb[rb] = s16x4{0, 0, 0, 0};
       lsum[rb] = 0.f;
     }
 
@@ -777,7 +809,7 @@ __global__ void __launch_bounds__(64 * kNW, 1) attn_bf16_kernel(AttnParams P) {
           mx[rb] = lane_max(sc[rb]);
           up |= mx[rb] > mst.thr[rb];
         }
-        if (__any(up)) raise_max<D, RB>(mx, mst, sc, lsum, o);
+        if (__any(up)) raise_max<D, RB>(mx, mst, sc, lsum, o, (int)(threadIdx.x & 63));
         softmax_p<RB>(sc, pk, lsum);
       };
       // the work-group's share of the tile traffic of step s: rotate and store
@@ -793,10 +825,10 @@ __global__ void __launch_bounds__(64 * kNW, 1) attn_bf16_kernel(AttnParams P) {
       };
       // S(s+1) = K(s+1) Q^T and O += V(s) P(s), with the row sums of P(s)
       auto mfma = [&](int s) {
-        qk_pv<D, RB>(cx, (s + 1) & 1, s & 1, qf, mst.bias, sc, pk, o);
+        qk_pv<D, RB>(cx, (s + 1) & 1, s & 1, qf, ones, mst.mb, sc, pk, o);
       };
       if constexpr (!prod) {
-        qk<D, RB>(cx, 0, qf, mst.bias, sc);
+        qk<D, RB>(cx, 0, qf, ones, mst.mb, sc);
         if (lead) softmax_step(0);
       }
       __syncthreads();   // K(0) read by every wave before step 0 reuses its buffer

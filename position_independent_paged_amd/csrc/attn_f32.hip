@@ -39,7 +39,9 @@ __global__ void __launch_bounds__(kNTf) attn_f32_kernel(AttnParams P) {
   }
   int q_cur = blockIdx.x % kQueues;   // queue being drained (thread 0)
   __syncthreads();
-  if (tid == 0) s_next = resolve_ticket(P.hdr, s_qs, s_qc, q_cur, atomicAdd(&P.hdr->next[q_cur], 1u));
+  // the first item is the work-group's own ticket (the planner starts each
+  // queue's counter past the work-groups that drain it)
+  if (tid == 0) s_next = resolve_ticket(P.hdr, s_qs, s_qc, q_cur, blockIdx.x / kQueues);
   __syncthreads();
   int it = __builtin_amdgcn_readfirstlane(s_next);
   while (it >= 0) {

@@ -73,7 +73,8 @@ struct WsHeader {
   uint32_t num_items;           // written by plan_items
   uint32_t chunk;               // key blocks per piece chosen by plan_items
   uint32_t num_groups;          // split (tile, KV head) groups listed for the merge
-  uint32_t next[kQueues];       // per-queue scheduler counters (zeroed by plan_items)
+  uint32_t next[kQueues];       // per-queue ticket counters (plan_items starts each past the
+                                // work-groups' own first tickets)
   uint32_t qstart[kQueues];     // first item of each queue
   uint32_t qcount[kQueues];     // items in each queue
   uint32_t pad[4];

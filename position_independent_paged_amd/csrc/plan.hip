@@ -459,7 +459,9 @@ __global__ void __launch_bounds__(kItemThreads) plan_items_kernel(PlanParams P) 
   if (tid < kQueues) {
     const uint32_t end = tid + 1 < kQueues ? (uint32_t)bins[(tid + 1) * kCostBins] : (uint32_t)total;
     P.hdr->qcount[tid] = end - (uint32_t)bins[tid * kCostBins];
-    P.hdr->next[tid] = 0u;
+    // tickets 0 .. (work-groups of the queue) - 1 are the work-groups' first
+    // items, taken without an atomic (work-group b: ticket b / 8 of queue b % 8)
+    P.hdr->next[tid] = P.num_wg > tid ? (uint32_t)((P.num_wg - tid + kQueues - 1) / kQueues) : 0u;
   }
   __syncthreads();
   int t_td = -1;
