@@ -337,8 +337,8 @@ __device__ __forceinline__ void qk(const StepCtx<D, RB>& cx, int buf, const bf16
 
 // S(s+1) = K Q^T from K buffer kbuf and O += V P from V buffer vbuf (one row
 // block per wave): the LDS fragment reads run kRing ahead of the MFMAs in a
-// ring (program order pinned with scheduling fences), so an MFMA seldom waits
-// on an LDS read.
+// ring (program order of the QK part pinned with scheduling fences), so an
+// MFMA seldom waits on an LDS read.
 constexpr int kRing = 2;
 template <int D, int RB>
 __device__ __forceinline__ void qk_pv(const StepCtx<D, RB>& cx, int kbuf, int vbuf, const bf16x8 (&qf)[RB][D / 16],
@@ -365,7 +365,9 @@ __device__ __forceinline__ void qk_pv(const StepCtx<D, RB>& cx, int kbuf, int vb
     if (i < NK) s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[0][i], s[0], 0, 0, 0);
     else o[0][(i - NK) / 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pk[0][(i - NK) % 2], o[0][(i - NK) / 2], 0, 0, 0);
     if (i + kRing < N) ring[i % kRing] = *addr(i + kRing);
-    __builtin_amdgcn_sched_barrier(0);
+    // the QK part in a pinned order; the PV part left to the scheduler, which
+    // may move the wave's other work between its MFMAs
+    if (i < NK) __builtin_amdgcn_sched_barrier(0);
   }
 }
 
