@@ -20,10 +20,15 @@
 //     whose B operand layout is the S accumulator's, and whose A operand is an
 //     8-byte read of the [d][16] V block;
 //   * the block table, span ids and flags are read through the scalar cache
-//     (the block index is wave-uniform), and each block's cos/sin rows are
-//     requested before the next block's K/V: the waits for a block's data
-//     never wait for the following block's loads, so one block stays in
-//     flight behind the one being computed;
+//     (the block index is wave-uniform; a PDep query, the usual decode case,
+//     sees every block up to its own and skips the scan), and each block's
+//     cos/sin rows are requested before the next block's K/V: the waits for a
+//     block's data never wait for the following block's loads, so one block
+//     stays in flight behind the one being computed. The K/V and position
+//     loads are buffer loads issued on every path (a descriptor without
+//     records reads zeros with no memory request past the split or for an
+//     invalid block): a load issued on one path only would make the
+//     compiler's wait at the join count it and wait for everything;
 //   * every wave writes its (O, m, l) partial (m in log2 units); a merge
 //     kernel combines the splits of a (request, query head) in split order.
 #include "common.h"
@@ -31,6 +36,14 @@
 namespace minipic {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Word 3 of a raw buffer resource on gfx9 (32-bit data, no swizzle, no
+// index stride). A load at an offset past num_records returns zeros and
+// sends no request to memory.
+constexpr int kBufWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kBufWord3);
+}
 
 template <int D, int G, bool ROPE>
 __global__ void __launch_bounds__(64) decode_bf16_kernel(DecodeParams P) {
@@ -133,6 +146,7 @@ __global__ void __launch_bounds__(64) decode_bf16_kernel(DecodeParams P) {
     // the next block of the split the query sees, or b1
     auto next_visible = [&](int b) {
       b = __builtin_amdgcn_readfirstlane(b);
+      if (pdep_q) return b;   // a PDep query sees every block up to its own
       bool broken = false;
       for (; b < b1; ++b) {
         const bool glob = (flg_at(b) & MINIPIC_BLK_GLOBAL) != 0;
@@ -147,35 +161,43 @@ __global__ void __launch_bounds__(64) decode_bf16_kernel(DecodeParams P) {
     // V^T operand: lane (n, j) = d row 16 mt + n, keys 4 j .. 4 j + 3; the
     // key's logical position. An invalid block reads as zeros.
     auto load_block = [&](int b, bf16x8 (&ka)[NC], s16x4 (&va)[NM], int& pos) {
-      // a key past the context holds no token: its position is not read (the
-      // lane then follows the block's run of positions, or reads row 0). It
-      // is loaded first, so that waiting for it waits for no K/V load.
-      pos = ROPE && b * kBlock + n < L ? lpos[b * kBlock + n] : 0;
-      int ph = ((const CI*)btab)[b];
-      if (ph < 0 || (int64_t)ph >= P.num_blocks) {
+      // Every load is issued, whatever the block: past the split or for an
+      // invalid block the buffer descriptors have no records, the loads
+      // read zeros without a memory request, and the waits for the next
+      // block count the same loads on every path.
+      const bool in = b < b1;
+      int ph = in ? ((const CI*)btab)[b] : -1;
+      if (in && (ph < 0 || (int64_t)ph >= P.num_blocks)) {
         if (l == 0) atomicOr(P.err, (uint32_t)MINIPIC_EW_BLOCK);
         ph = -1;
       }
-      if (ph >= 0) {
-        const __bf16* kr = kc + ph * group + n * D + 8 * j;
-#pragma unroll
-        for (int t = 0; t < NC; ++t) ka[t] = *(const bf16x8*)(kr + 32 * t);
-        const __bf16* vr = vc + ph * group + n * kBlock + 4 * j;
-#pragma unroll
-        for (int mt = 0; mt < NM; ++mt) va[mt] = *(const s16x4*)(vr + 16 * mt * kBlock);
+      // a key past the context holds no token: its position is not read (the
+      // lane then follows the block's run of positions, or reads row 0). It
+      // is loaded first, so that waiting for it waits for no K/V load.
+      if (ROPE) {
+        const int live = __builtin_amdgcn_readfirstlane(in ? min(max(L - b * kBlock, 0), kBlock) : 0);
+        const __amdgpu_buffer_rsrc_t rp = buf_rsrc(lpos + (live > 0 ? (int64_t)b * kBlock : 0), 4 * live);
+        pos = __builtin_amdgcn_raw_buffer_load_b32(rp, 4 * n, 0, 0);
       } else {
-#pragma unroll
-        for (int t = 0; t < NC; ++t) ka[t] = bf16x8{};
-#pragma unroll
-        for (int mt = 0; mt < NM; ++mt) va[mt] = s16x4{0, 0, 0, 0};
+        pos = 0;
       }
+      ph = __builtin_amdgcn_readfirstlane(ph);   // uniform: the descriptors live in scalar registers
+      const int64_t off = ph >= 0 ? (int64_t)ph * group : 0;
+      const __amdgpu_buffer_rsrc_t rk = buf_rsrc(kc + off, ph >= 0 ? kBlock * D * 2 : 0);
+      const __amdgpu_buffer_rsrc_t rv = buf_rsrc(vc + off, ph >= 0 ? kBlock * D * 2 : 0);
+#pragma unroll
+      for (int t = 0; t < NC; ++t)
+        ka[t] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rk, 2 * (n * D + 8 * j + 32 * t), 0, 0));
+#pragma unroll
+      for (int mt = 0; mt < NM; ++mt)
+        va[mt] = __builtin_bit_cast(s16x4, __builtin_amdgcn_raw_buffer_load_b64(rv, 2 * (n * kBlock + 4 * j + 16 * mt * kBlock), 0, 0));
     };
     // one block in flight ahead of the one being computed
     bf16x8 ka_n[NC];
     s16x4 va_n[NM];
     int pos_n = 0;
     int b = next_visible(b0);
-    if (b < b1) load_block(b, ka_n, va_n, pos_n);
+    load_block(b, ka_n, va_n, pos_n);
     while (b < b1) {
       bf16x8 ka[NC];
       s16x4 va[NM];
@@ -210,7 +232,7 @@ __global__ void __launch_bounds__(64) decode_bf16_kernel(DecodeParams P) {
         }
       }
       b = next_visible(b + 1);
-      if (b < b1) load_block(b, ka_n, va_n, pos_n);
+      load_block(b, ka_n, va_n, pos_n);
       if (ROPE) {
         // rotate-half at the key's logical position: element i (first half)
         // with element i + D/2, in fp32, one rounding to bf16
