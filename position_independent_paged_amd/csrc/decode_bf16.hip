@@ -325,14 +325,17 @@ __global__ void __launch_bounds__(64) decode_bf16_kernel(DecodeParams P) {
 // sum_s 2^(m_s - m*) l_s, m* = max_s m_s. One 256-thread work-group per
 // (request, query head, slice of 32 E elements of d): E = D / 32 (whole
 // rows) for batches of many requests, E = 1 where few (request, head) pairs
-// would leave most of the GPU idle. The split weights are computed in
-// parallel into LDS; the eight 32-lane groups sum splits g, g + 8, ... of the
-// slice (E consecutive elements per lane), and the eight partial sums are
-// added in group order.
+// would leave most of the GPU idle. The (m, l) pairs of the splits go to LDS
+// in one pass; the first batch of partial outputs is requested right after
+// them, so its latency passes while the max, the weights and the denominator
+// are formed. The eight 32-lane groups sum splits g, g + 8, ... of the slice
+// (E consecutive elements per lane, 32 / E splits in flight per lane), and
+// the eight partial sums are added in group order.
 template <int D, int E>
 __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeParams P, int G) {
   constexpr int NDC = D / (32 * E);   // slices of d
-  __shared__ float w_s[kDecodeMaxSplits];
+  constexpr int UNR = 32 / E;         // splits per lane and batch
+  __shared__ float2 ml_s[kDecodeMaxSplits];
   __shared__ float red[256 / 64][2];
   __shared__ float part[8][32 * E];
   const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
@@ -344,7 +347,22 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeParams P, int G
   const int ns = P.nsplit;
   const int64_t base = (int64_t)(r * P.hkv + g) * ns * G + n;   // split s at base + s G
   float mloc = -INFINITY;
-  for (int s = tid; s < ns; s += 256) mloc = fmaxf(mloc, P.part_ml[base + (int64_t)s * G].x);
+  for (int s = tid; s < ns; s += 256) {
+    const float2 ml = P.part_ml[base + (int64_t)s * G];
+    ml_s[s] = ml;
+    mloc = fmaxf(mloc, ml.x);
+  }
+  const float* po = P.part_o + base * D + 32 * E * dc + E * e;
+  float v[UNR][E];
+  auto load_batch = [&](int s0) {
+#pragma unroll
+    for (int k = 0; k < UNR; ++k) {
+      const int s = s0 + 8 * k;
+#pragma unroll
+      for (int i = 0; i < E; ++i) v[k][i] = s < ns ? po[(int64_t)s * G * D + i] : 0.f;
+    }
+  };
+  load_batch(grp);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, o, 64));
   if (l == 0) red[w][0] = mloc;
@@ -352,9 +370,9 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeParams P, int G
   const float mstar = fmaxf(fmaxf(red[0][0], red[1][0]), fmaxf(red[2][0], red[3][0]));
   float dloc = 0.f;
   for (int s = tid; s < ns; s += 256) {
-    const float2 ml = P.part_ml[base + (int64_t)s * G];
+    const float2 ml = ml_s[s];
     const float wt = ml.x == -INFINITY ? 0.f : exp2f(ml.x - mstar);
-    w_s[s] = wt;
+    ml_s[s].x = wt;
     dloc += wt * ml.y;
   }
 #pragma unroll
@@ -362,23 +380,15 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeParams P, int G
   if (l == 0) red[w][1] = dloc;
   __syncthreads();
   const float den = (red[0][1] + red[1][1]) + (red[2][1] + red[3][1]);
-  constexpr int UNR = 4;
   float num[E];
 #pragma unroll
   for (int i = 0; i < E; ++i) num[i] = 0.f;
-  const float* po = P.part_o + base * D + 32 * E * dc + E * e;
   for (int s0 = grp; s0 < ns; s0 += 8 * UNR) {
-    float v[UNR][E];
+    if (s0 != grp) load_batch(s0);
 #pragma unroll
     for (int k = 0; k < UNR; ++k) {
       const int s = s0 + 8 * k;
-#pragma unroll
-      for (int i = 0; i < E; ++i) v[k][i] = s < ns ? po[(int64_t)s * G * D + i] : 0.f;
-    }
-#pragma unroll
-    for (int k = 0; k < UNR; ++k) {
-      const int s = s0 + 8 * k;
-      const float wt = s < ns ? w_s[s] : 0.f;
+      const float wt = s < ns ? ml_s[s].x : 0.f;
 #pragma unroll
       for (int i = 0; i < E; ++i) num[i] += wt * v[k][i];
     }
