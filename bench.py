@@ -369,6 +369,9 @@ def decode_entry(name, reps):
     # the few microseconds that events around every launch add to such short kernels
     call_ms = calls_ms(dw.decode, 10 * reps)
     call_ms_prerot = calls_ms(dw.decode_prerotated, 10 * reps)
+    # whole calls replayed from a captured HIP graph: the GPU's time per call, free of the host's launch rate
+    graph = graph_steps(dw.decode, call_ms, reps=5)["ms_per_step_median"]
+    graph_prerot = graph_steps(dw.decode_prerotated, call_ms_prerot, reps=5)["ms_per_step_median"]
     e = {"workload": f"decode step after {name.replace('d', 'c', 1)}: one query row per request (its last "
                      f"context token)", "requests": int(w.num_reqs), "context_tokens": int(w.ctx_len.sum()),
          "algorithmic_MB": round(nbytes / 1e6, 2), "decode_kernel_ms": round(attn, 5),
@@ -377,7 +380,10 @@ def decode_entry(name, reps):
          "rope_overhead_pct": round(100 * (attn / prerot - 1), 2),
          "call_ms_back_to_back": round(call_ms, 5), "prerotated_call_ms_back_to_back": round(call_ms_prerot, 5),
          "GBps_call_back_to_back": round(nbytes / (call_ms * 1e-3) / 1e9, 1),
-         "rope_overhead_call_pct": round(100 * (call_ms / call_ms_prerot - 1), 2)}
+         "rope_overhead_call_pct": round(100 * (call_ms / call_ms_prerot - 1), 2),
+         "call_ms_graph_replay": graph, "prerotated_call_ms_graph_replay": graph_prerot,
+         "GBps_call_graph_replay": round(nbytes / (graph * 1e-3) / 1e9, 1),
+         "rope_overhead_graph_pct": round(100 * (graph / graph_prerot - 1), 2)}
     del dw
     torch.cuda.empty_cache()
     return e
@@ -597,7 +603,9 @@ def main():
         if "decode_kernel_ms" in e:
             log(f"[bench] suite {name}: decode {e['decode_kernel_ms']:.4f} ms, {e['GBps_kernel']:.0f} GB/s, "
                 f"RoPE +{e['rope_overhead_pct']:.1f}%; back-to-back calls {e['call_ms_back_to_back']:.4f} ms "
-                f"(with merge), RoPE +{e['rope_overhead_call_pct']:.1f}%")
+                f"(with merge), RoPE +{e['rope_overhead_call_pct']:.1f}%; graph-replayed calls "
+                f"{e['call_ms_graph_replay']:.4f} ms ({e['GBps_call_graph_replay']:.0f} GB/s), "
+                f"RoPE +{e['rope_overhead_graph_pct']:.1f}%")
         else:
             log(f"[bench] suite {name}: {e['attention_kernel_ms']:.4f} ms, {e['tflops_kernel']:.1f} TFLOP/s, "
                 f"RoPE +{e['rope_overhead_pct']:.1f}%")

@@ -305,3 +305,36 @@ def test_piece_doubling_path(name, monkeypatch):
     check(f"doubling/{name}", got, oracle_all(w), w.dtype)
     # fewer, longer pieces: the same result up to the order of the fp32 sums
     assert np.abs(got - out_f64(ref)).max() <= (1e-5 if w.dtype == "f32" else 2e-2)
+
+
+@pytest.mark.parametrize("name", ["d3_small", "d5_small"])
+def test_graph_replay_matches_eager_decode(name):
+    """Decode (split attention + merge) captured in a HIP graph: every replay,
+    with eager calls between them, gives the eager output bit for bit."""
+    w = workload.make_config(name)
+    say(f"graph replay decode {name}")
+    dw = stage(w)
+    dw.write_new()
+    dw.decode()
+    torch.cuda.synchronize()
+    ref = dw.out.clone()
+    other = torch.empty_like(dw.out)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        dw.decode()                     # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        dw.decode()
+        dw.decode()
+    for i in range(4):
+        dw.out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(dw.out.view(torch.int16), ref.view(torch.int16)), f"replay {i}"
+        dw.decode(out=other)            # eager work between the replays
+        torch.cuda.synchronize()
+        assert torch.equal(other.view(torch.int16), ref.view(torch.int16)), f"eager {i}"
+    assert dw.decode_error_word() == 0
