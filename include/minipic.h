@@ -62,6 +62,8 @@ extern "C" {
 #define MINIPIC_EW_CTX     8u  /* ctx_len exceeded max_blocks_per_req * block_size */
 #define MINIPIC_EW_SPAN   16u  /* a query's span id also names a block before its own run
                                   (the span-id contract of minipic_batch is broken) */
+#define MINIPIC_EW_PLAN   32u  /* minipic_prefill_run found no plan of its configuration
+                                  in the workspace (nothing was computed) */
 
 /*
  * One batch of prefill requests. Host scalars plus device arrays.
@@ -233,6 +235,39 @@ int minipic_reference_prerotated(const void* q, const void* k_cache, const void*
                                  const float* cos_sin, int32_t max_pos, float softmax_scale,
                                  void* out, void* workspace, size_t workspace_bytes,
                                  uint32_t flags, int32_t dtype, void* stream);
+
+/*
+ * minipic_prefill_attn in two parts, for a model that runs the same batch
+ * through many layers: the work decomposition of the position-free paged
+ * attention ("MiniPIC ...", §3.2.1 and §3.2.2: which key blocks each query
+ * tile sees, the pieces long key lists are cut into, their queues and the
+ * split groups to merge) depends only on the batch's descriptors, not on q or
+ * the caches, so it can be built once and used by every layer.
+ *   minipic_prefill_plan : launches the planning kernels only. Arguments as
+ *              for minipic_prefill_attn (q, the caches and out are not taken;
+ *              num_blocks, cos_sin / max_pos and flags are, since the plan
+ *              checks block numbers and key positions against them).
+ *   minipic_prefill_run  : launches the attention and merge kernels on a
+ *              workspace that holds a plan of the same batch, made by
+ *              minipic_prefill_plan with the same num_blocks, cos_sin,
+ *              max_pos, flags and dtype on the same device (the caller
+ *              keeps the batch's device arrays unchanged in between). Its
+ *              results are those of minipic_prefill_attn, bit for bit. The
+ *              run leaves the plan ready for the next run (the merge kernel
+ *              re-arms the scheduler's counters), so one plan serves any
+ *              number of runs in order on one stream.
+ * The plan records a key of its configuration in the workspace (the scalars
+ * above, the batch's scalars and array addresses, the launch size); a run
+ * whose key differs computes nothing, leaves out untouched and sets
+ * MINIPIC_EW_PLAN in the error word. Host-side errors are returned as by
+ * minipic_prefill_attn. Runs and plans on one workspace must not overlap.
+ */
+int minipic_prefill_plan(int64_t num_blocks, const minipic_batch* batch, const float* cos_sin, int32_t max_pos,
+                         void* workspace, size_t workspace_bytes, uint32_t flags, int32_t dtype, void* stream);
+int minipic_prefill_run(const void* q, const void* k_cache, const void* v_cache, int64_t num_blocks,
+                        const minipic_batch* batch, const float* cos_sin, int32_t max_pos,
+                        float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+                        uint32_t flags, int32_t dtype, void* stream);
 
 /*
  * Decode-phase position-free paged attention: one query row per request

@@ -11,7 +11,8 @@ from ._binding import (BlockCache, MINIPIC_ERR_CACHE_FULL, MINIPIC_ERR_CONTRACT,
                        LIB_PATH, MinipicError, load_library, minipic_batch, minipic_get_launch_info,
                        minipic_decode_attn, minipic_decode_prerotated, minipic_decode_workspace_size,
                        minipic_kernel_times, minipic_kernel_times_all, minipic_prefill_attn,
-                       minipic_prefill_attn_static, MINIPIC_STATIC_WORKSPACE_BYTES,
+                       minipic_prefill_attn_static, MINIPIC_STATIC_WORKSPACE_BYTES, minipic_prefill_plan,
+                       minipic_prefill_run, MINIPIC_EW_SPAN, MINIPIC_EW_PLAN,
                        minipic_reference_prerotated,
                        minipic_rope_table, minipic_set_kernel_timing, minipic_version, minipic_workspace_size,
                        minipic_write_kv)
@@ -21,6 +22,7 @@ __all__ = [
     "BlockCache", "MINIPIC_ERR_CACHE_FULL", "MINIPIC_ERR_CONTRACT", "minipic_describe_blocks", "minipic_slot_mapping",
     "EXPORTS", "LIB_PATH", "MinipicError", "load_library", "minipic_batch", "minipic_get_launch_info",
     "minipic_prefill_attn", "minipic_prefill_attn_static", "MINIPIC_STATIC_WORKSPACE_BYTES",
+    "minipic_prefill_plan", "minipic_prefill_run", "MINIPIC_EW_SPAN", "MINIPIC_EW_PLAN",
     "minipic_reference_prerotated", "minipic_rope_table", "minipic_version",
     "minipic_set_kernel_timing", "minipic_kernel_times", "minipic_kernel_times_all", "minipic_decode_workspace_size",
     "minipic_decode_attn", "minipic_decode_prerotated",

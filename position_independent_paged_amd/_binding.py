@@ -24,6 +24,8 @@ MINIPIC_EW_BLOCK = 1
 MINIPIC_EW_POS = 2
 MINIPIC_EW_QCTX = 4
 MINIPIC_EW_CTX = 8
+MINIPIC_EW_SPAN = 16
+MINIPIC_EW_PLAN = 32
 
 EXPORTS = [
     "minipic_version", "minipic_status_string", "minipic_last_error", "minipic_rope_table",
@@ -33,6 +35,7 @@ EXPORTS = [
     "minipic_decode_workspace_size", "minipic_decode_attn", "minipic_decode_prerotated",
     "minipic_describe_blocks", "minipic_block_cache_create", "minipic_block_cache_destroy",
     "minipic_block_cache_assign", "minipic_slot_mapping", "minipic_prefill_attn_static",
+    "minipic_prefill_plan", "minipic_prefill_run",
 ]
 
 
@@ -103,6 +106,9 @@ def load_library(path: str = None):
             i32, vp]
     lib.minipic_prefill_attn.argtypes = attn
     lib.minipic_reference_prerotated.argtypes = attn
+    lib.minipic_prefill_run.argtypes = attn
+    lib.minipic_prefill_plan.argtypes = [i64, ctypes.POINTER(minipic_batch), vp, i32, vp, sz, ctypes.c_uint32, i32,
+                                         vp]
     lib.minipic_prefill_attn_static.argtypes = [vp, vp, vp, i64, ctypes.POINTER(minipic_batch), vp, i32,
                                                 ctypes.c_float, vp, vp, ctypes.c_uint32, i32, vp]
     lib.minipic_decode_workspace_size.argtypes = [ctypes.POINTER(minipic_batch), i32, ctypes.POINTER(sz)]
@@ -192,6 +198,22 @@ def _attn(fn, q, k_cache, v_cache, num_blocks, batch, cos_sin, max_pos, out, wor
 def minipic_prefill_attn(q, k_cache, v_cache, num_blocks, batch, cos_sin, max_pos, out, workspace, *,
                          flags: int = 0, softmax_scale: float = 0.0, stream=None):
     _attn(load_library().minipic_prefill_attn, q, k_cache, v_cache, num_blocks, batch, cos_sin, max_pos, out,
+          workspace, flags, softmax_scale, stream)
+
+
+def minipic_prefill_plan(num_blocks, batch, cos_sin, max_pos, workspace, *, dtype_code: int, flags: int = 0,
+                         stream=None):
+    """The planning kernels of minipic_prefill_attn only (the plan serves minipic_prefill_run calls)."""
+    _check(load_library().minipic_prefill_plan(
+        int(num_blocks), ctypes.byref(batch), _ptr(cos_sin), int(max_pos), _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), int(flags), int(dtype_code),
+        _stream(stream)))
+
+
+def minipic_prefill_run(q, k_cache, v_cache, num_blocks, batch, cos_sin, max_pos, out, workspace, *,
+                        flags: int = 0, softmax_scale: float = 0.0, stream=None):
+    """The attention and merge kernels of minipic_prefill_attn on a workspace holding a plan of the batch."""
+    _attn(load_library().minipic_prefill_run, q, k_cache, v_cache, num_blocks, batch, cos_sin, max_pos, out,
           workspace, flags, softmax_scale, stream)
 
 

@@ -535,6 +535,11 @@ __global__ void __launch_bounds__(64 * kNW, 1) attn_bf16_kernel(AttnParams P) {
   const float sl2 = P.scale_log2;
   const rsrc_t tab = make_rsrc(P.cos_sin, P.max_pos * D * 4);
 
+  // a run needs the plan of its own configuration in the workspace
+  if (P.hdr->plan_key != P.plan_key) {   // uniform (one scalar load)
+    if (blockIdx.x == 0 && tid == 0) atomicOr(P.err, (uint32_t)MINIPIC_EW_PLAN);
+    return;
+  }
   if (blockIdx.x == 0 && tid == 0) {   // measurement: clock stamps of work-group 0
     P.hdr->clk_start = clock64();
     P.hdr->rt_start = wall_clock64();

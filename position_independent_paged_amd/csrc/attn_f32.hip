@@ -33,6 +33,11 @@ __global__ void __launch_bounds__(kNTf) attn_f32_kernel(AttnParams P) {
   const float sl2 = P.scale_log2;
   const float* kc = (const float*)P.k_cache;
   const float* vc = (const float*)P.v_cache;
+  // a run needs the plan of its own configuration in the workspace
+  if (P.hdr->plan_key != P.plan_key) {   // uniform (one scalar load)
+    if (blockIdx.x == 0 && tid == 0) atomicOr(P.err, (uint32_t)MINIPIC_EW_PLAN);
+    return;
+  }
   if (tid < kQueues) {
     s_qs[tid] = P.hdr->qstart[tid];
     s_qc[tid] = P.hdr->qcount[tid];

@@ -130,6 +130,8 @@ hipError_t launch_rope_table(float* cs, int max_pos, int d, double base, hipStre
 // by D/4 threads (4 elements each). The piece weights are computed lane-
 // parallel (each lane owns pieces lane, lane + D/4, ...) into LDS, then the
 // numerator sums the pieces in piece order with several loads in flight.
+// The kernel also re-arms the attention scheduler's queue counters, which
+// leaves the plan in the workspace ready for another attention run.
 // ---------------------------------------------------------------------------
 template <typename T, int D, int ROWS>
 __global__ void __launch_bounds__(256) merge_kernel(AttnParams P, int G) {
@@ -139,6 +141,10 @@ __global__ void __launch_bounds__(256) merge_kernel(AttnParams P, int G) {
   constexpr int KP = kMaxSplits / TPR;   // pieces per lane in the weight pass
   constexpr int UNR = 8;                 // pieces loaded together
   __shared__ float w_s[RPW][kMaxSplits];
+  if (P.hdr->plan_key != P.plan_key) return;   // no plan of this run (uniform)
+  // The attention kernel has finished (stream order): re-arm the scheduler's
+  // counters, so that the plan serves the next run as well.
+  if (blockIdx.x == 0 && threadIdx.x < kQueues) P.hdr->next[threadIdx.x] = first_tickets(P.num_wg, threadIdx.x);
   const int ngroups = (int)P.hdr->num_groups;
   const int r_in = threadIdx.x / TPR;
   const int d4 = threadIdx.x % TPR;

@@ -77,7 +77,10 @@ struct WsHeader {
                                 // work-groups' own first tickets)
   uint32_t qstart[kQueues];     // first item of each queue
   uint32_t qcount[kQueues];     // items in each queue
-  uint32_t pad[4];
+  uint64_t plan_key;            // configuration the plan was built for (written by plan_items;
+                                // the attention and merge kernels run only on a matching plan;
+                                // never 0)
+  uint32_t pad[2];
   // Measurement: the attention kernel's work-group 0 stores the shader clock
   // counter and the 100 MHz real-time counter when it starts and when it has
   // drained the queues (the ratio of the differences is the shader clock).
@@ -85,6 +88,7 @@ struct WsHeader {
 };
 static_assert(sizeof(WsHeader) <= 256, "workspace header");
 static_assert(offsetof(WsHeader, clk_start) == 128, "clock stamps at byte 128 of the workspace");
+static_assert(offsetof(WsHeader, plan_key) % 8 == 0, "aligned plan key");
 
 // One split (tile, KV head): its pieces occupy slots slot0 .. slot0+nsplit-1.
 struct Group {
@@ -176,6 +180,7 @@ struct PlanParams {
   int32_t min_chunk;   // smallest piece (key blocks)
   const int32_t* logical_pos;
   int32_t max_pos;     // rows of the cos/sin table (1 when no table is used)
+  uint64_t plan_key;   // configuration key stored with the plan
 };
 
 // Parameters of the attention kernels.
@@ -202,7 +207,15 @@ struct AttnParams {
   int32_t max_groups;  // capacity of the group list
   float scale_log2;    // softmax_scale * log2(e)
   uint32_t flags;
+  uint64_t plan_key;   // configuration key the plan in the workspace must carry
+  int32_t num_wg;      // persistent attention work-groups
 };
+
+// Tickets a queue's counter starts past: work-group b takes ticket b / kQueues
+// of queue b % kQueues as its first item without an atomic.
+__device__ __forceinline__ uint32_t first_tickets(int num_wg, int q) {
+  return num_wg > q ? (uint32_t)((num_wg - q + kQueues - 1) / kQueues) : 0u;
+}
 
 // Parameters of the decode kernels (one query row per request).
 struct DecodeParams {

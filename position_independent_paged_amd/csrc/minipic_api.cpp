@@ -343,10 +343,53 @@ int persistent_grid(int dtype, int D, int G, bool rope, int* grid) {
   return 0;
 }
 
+// Key of a plan's configuration: FNV-1a over everything the planning kernels
+// read or size their output by (the batch's scalars and array addresses,
+// num_blocks, the table rows and flags, the dtype, the kernel variant and the
+// launch size). Never 0, so a zeroed workspace holds no plan.
+uint64_t plan_key(const minipic_batch* b, int32_t dtype, bool rope, uint32_t flags, int32_t max_pos_used,
+                  int64_t num_blocks, int grid) {
+  uint64_t h = 1469598103934665603ull;
+  auto mix = [&](uint64_t v) {
+    for (int i = 0; i < 8; ++i) {
+      h ^= (v >> (8 * i)) & 0xffu;
+      h *= 1099511628211ull;
+    }
+  };
+  mix((uint64_t)(uint32_t)dtype);
+  mix(rope ? 1u : 0u);
+  mix(flags);
+  mix((uint64_t)(uint32_t)max_pos_used);
+  mix((uint64_t)num_blocks);
+  mix((uint64_t)(uint32_t)grid);
+  mix((uint64_t)(uint32_t)b->num_reqs);
+  mix((uint64_t)(uint32_t)b->num_q_heads);
+  mix((uint64_t)(uint32_t)b->num_kv_heads);
+  mix((uint64_t)(uint32_t)b->head_dim);
+  mix((uint64_t)(uint32_t)b->block_size);
+  mix((uint64_t)(uint32_t)b->max_blocks_per_req);
+  mix((uint64_t)b->total_q);
+  mix((uint64_t)(uint32_t)b->max_q_len);
+  mix((uint64_t)(uintptr_t)b->q_indptr);
+  mix((uint64_t)(uintptr_t)b->q_ctx_idx);
+  mix((uint64_t)(uintptr_t)b->ctx_len);
+  mix((uint64_t)(uintptr_t)b->block_table);
+  mix((uint64_t)(uintptr_t)b->logical_pos);
+  mix((uint64_t)(uintptr_t)b->span_id);
+  mix((uint64_t)(uintptr_t)b->blk_flags);
+  return h == 0 ? 1 : h;
+}
+
+// What a prefill entry point launches: the planning kernels, the attention
+// and merge kernels, or both.
+enum class Mode { kPlanAndRun, kPlan, kRun };
+
 int run_attention(const void* q, const void* k_cache, const void* v_cache, int64_t num_blocks,
                   const minipic_batch* b, const float* cos_sin, int32_t max_pos, float softmax_scale,
                   void* out, void* workspace, size_t workspace_bytes, uint32_t flags, int32_t dtype,
-                  void* stream, bool rope, bool static_ws = false, uint32_t* err_word = nullptr) {
+                  void* stream, bool rope, bool static_ws = false, uint32_t* err_word = nullptr,
+                  Mode mode = Mode::kPlanAndRun) {
+  const bool do_plan = mode != Mode::kRun, do_run = mode != Mode::kPlan;
   int st = check_batch(b, dtype);
   if (st) return st;
   if (flags & ~(uint32_t)MINIPIC_FLAG_ROTATE_Q) return fail(MINIPIC_ERR_INVALID_ARG, "unknown flag bits 0x%x", flags);
@@ -357,10 +400,12 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, int64
     if (st) return st;
   }
   if (b->num_reqs == 0 || b->total_q == 0) return MINIPIC_OK;
-  if (!q || !out) return fail(MINIPIC_ERR_INVALID_ARG, "q or out is NULL");
-  if (!k_cache || !v_cache) return fail(MINIPIC_ERR_INVALID_ARG, "k_cache or v_cache is NULL");
+  if (do_run) {
+    if (!q || !out) return fail(MINIPIC_ERR_INVALID_ARG, "q or out is NULL");
+    if (!k_cache || !v_cache) return fail(MINIPIC_ERR_INVALID_ARG, "k_cache or v_cache is NULL");
+  }
   if (num_blocks == 0) return fail(MINIPIC_ERR_INVALID_ARG, "num_blocks is 0");
-  if (!(softmax_scale == softmax_scale) || std::isinf(softmax_scale))
+  if (do_run && (!(softmax_scale == softmax_scale) || std::isinf(softmax_scale)))
     return fail(MINIPIC_ERR_INVALID_ARG, "softmax_scale is not finite");
   Plan pl;
   make_plan(b, dtype, &pl);
@@ -416,6 +461,7 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, int64
   Q.min_chunk = pl.min_chunk;
   Q.logical_pos = b->logical_pos;
   Q.max_pos = need_table ? max_pos : 1;
+  Q.plan_key = plan_key(b, dtype, rope, flags, Q.max_pos, num_blocks, grid);
 
   AttnParams P{};
   P.q = q;
@@ -441,13 +487,19 @@ int run_attention(const void* q, const void* k_cache, const void* v_cache, int64
   const float scale = softmax_scale > 0.f ? softmax_scale : 1.0f / std::sqrt((float)b->head_dim);
   P.scale_log2 = scale * 1.4426950408889634f;
   P.flags = flags;
+  P.plan_key = Q.plan_key;
+  P.num_wg = grid;
   hipStream_t s = (hipStream_t)stream;
   // calls on the static workspace record no timing events (creating them allocates)
   const bool timed = !static_ws;
   auto mark = [&](int i) { return timed ? timer_mark(i, s) : hipSuccess; };
   if (timed) g_timer.valid = false;
+  if (mode == Mode::kPlan) {
+    hipError_t e = launch_plan(Q, pl.bq, s);
+    return e == hipSuccess ? MINIPIC_OK : hip_fail(e, "plan launch");
+  }
   hipError_t e = mark(0);
-  if (e == hipSuccess) e = launch_plan(Q, pl.bq, s);
+  if (e == hipSuccess && do_plan) e = launch_plan(Q, pl.bq, s);
   if (e != hipSuccess) return hip_fail(e, "plan launch");
   e = mark(1);
   if (e == hipSuccess)
@@ -564,6 +616,18 @@ int minipic_prefill_attn_static(const void* q, const void* k_cache, const void* 
                        flags, dtype, stream, /*rope=*/true, /*static_ws=*/true, err_word);
 }
 
+int minipic_prefill_plan(int64_t num_blocks, const minipic_batch* batch, const float* cos_sin, int32_t max_pos,
+                         void* workspace, size_t workspace_bytes, uint32_t flags, int32_t dtype, void* stream) {
+  return run_attention(nullptr, nullptr, nullptr, num_blocks, batch, cos_sin, max_pos, 0.f, nullptr, workspace,
+                       workspace_bytes, flags, dtype, stream, /*rope=*/true, false, nullptr, Mode::kPlan);
+}
+int minipic_prefill_run(const void* q, const void* k_cache, const void* v_cache, int64_t num_blocks,
+                        const minipic_batch* batch, const float* cos_sin, int32_t max_pos, float softmax_scale,
+                        void* out, void* workspace, size_t workspace_bytes, uint32_t flags, int32_t dtype,
+                        void* stream) {
+  return run_attention(q, k_cache, v_cache, num_blocks, batch, cos_sin, max_pos, softmax_scale, out, workspace,
+                       workspace_bytes, flags, dtype, stream, /*rope=*/true, false, nullptr, Mode::kRun);
+}
 int minipic_reference_prerotated(const void* q, const void* k_cache, const void* v_cache, int64_t num_blocks,
                                  const minipic_batch* batch, const float* cos_sin, int32_t max_pos,
                                  float softmax_scale, void* out, void* workspace, size_t workspace_bytes,

@@ -10,8 +10,9 @@
 // and the number of persistent attention work-groups, cuts long tile lists
 // into pieces, assigns partial-result slots, and writes the work items
 // (tile, KV head, piece) into per-XCD queues, longest first, and the list of
-// split (tile, KV head) groups for the merge. It also zeroes the scheduler
-// counter, so the attention kernel needs no host-side memset.
+// split (tile, KV head) groups for the merge. It also starts the scheduler's
+// queue counters (so the attention kernel needs no host-side memset) and
+// records the configuration key the attention and merge kernels check.
 #include <climits>
 
 #include "common.h"
@@ -461,7 +462,7 @@ __global__ void __launch_bounds__(kItemThreads) plan_items_kernel(PlanParams P) 
     P.hdr->qcount[tid] = end - (uint32_t)bins[tid * kCostBins];
     // tickets 0 .. (work-groups of the queue) - 1 are the work-groups' first
     // items, taken without an atomic (work-group b: ticket b / 8 of queue b % 8)
-    P.hdr->next[tid] = P.num_wg > tid ? (uint32_t)((P.num_wg - tid + kQueues - 1) / kQueues) : 0u;
+    P.hdr->next[tid] = first_tickets(P.num_wg, tid);
   }
   __syncthreads();
   int t_td = -1;
@@ -502,6 +503,7 @@ __global__ void __launch_bounds__(kItemThreads) plan_items_kernel(PlanParams P) 
     P.hdr->num_items = (uint32_t)total;
     P.hdr->chunk = (uint32_t)chunk;
     P.hdr->num_groups = (uint32_t)group_base;
+    P.hdr->plan_key = P.plan_key;
   }
 }
 

@@ -14,7 +14,8 @@ import numpy as np
 import torch
 
 from ._binding import (MINIPIC_BF16, MINIPIC_F32, minipic_batch, minipic_get_launch_info,
-                       minipic_prefill_attn, minipic_reference_prerotated, minipic_rope_table,
+                       minipic_prefill_attn, minipic_prefill_plan, minipic_prefill_run,
+                       minipic_reference_prerotated, minipic_rope_table,
                        minipic_workspace_size, minipic_write_kv, minipic_decode_attn,
                        minipic_decode_prerotated, minipic_decode_workspace_size)
 
@@ -116,6 +117,18 @@ class DeviceWorkload:
         minipic_prefill_attn(self.q if q is None else q, self.k_cache, self.v_cache, self.num_blocks,
                              self.batch.struct, self.cos_sin, self.max_pos, self.out if out is None else out,
                              self.workspace, flags=self.flags if flags is None else flags)
+
+    def plan(self, flags=None):
+        """The planning kernels only: the plan in the workspace serves run() calls."""
+        minipic_prefill_plan(self.num_blocks, self.batch.struct, self.cos_sin, self.max_pos, self.workspace,
+                             dtype_code=self.dtype_code, flags=self.flags if flags is None else flags)
+
+    def run(self, out=None, flags=None, q=None, k_cache=None, v_cache=None):
+        """Attention and merge on the plan made by plan() (as attend(), without planning)."""
+        minipic_prefill_run(self.q if q is None else q, self.k_cache if k_cache is None else k_cache,
+                            self.v_cache if v_cache is None else v_cache, self.num_blocks, self.batch.struct,
+                            self.cos_sin, self.max_pos, self.out if out is None else out, self.workspace,
+                            flags=self.flags if flags is None else flags)
 
     def attend_prerotated(self, out=None, flags=None, k_cache=None, q=None):
         minipic_reference_prerotated(self.q if q is None else q, self.k_cache if k_cache is None else k_cache,

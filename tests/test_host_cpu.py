@@ -97,6 +97,38 @@ def test_attention_rejects_bad_buffers():
     assert _attn(b, table=None, max_pos=0, ws_bytes=64, rope=False) == -3
 
 
+def _plan(b, dtype=1, ws_bytes=1 << 30, ws=256, table=256, max_pos=1024, flags=0, num_blocks=10):
+    return pip.load_library().minipic_prefill_plan(num_blocks, ctypes.byref(b), table, max_pos, ws, ws_bytes, flags,
+                                                  dtype, None)
+
+
+def _run(b, dtype=1, ws_bytes=1 << 30, q=256, out=256, ws=256, table=256, max_pos=1024, flags=0):
+    return pip.load_library().minipic_prefill_run(q, 256, 256, 10, ctypes.byref(b), table, max_pos, 0.0, out, ws,
+                                                 ws_bytes, flags, dtype, None)
+
+
+def test_plan_and_run_validate_like_the_whole_call():
+    # every check runs on the host before any HIP call, as for minipic_prefill_attn
+    b = _batch()
+    for fn in (_plan, _run):
+        assert fn(_batch(head_dim=96)) == -2
+        assert fn(_batch(num_reqs=-1)) == -1
+        assert fn(b, dtype=7) == -2
+        assert fn(b, table=None) == -1
+        assert fn(b, max_pos=0) == -1
+        assert fn(b, flags=0x10) == -1
+        assert fn(b, ws=None) == -1
+        assert fn(b, ws=256 + 4) == -1
+        assert fn(b, ws_bytes=64) == -3
+        assert fn(_batch(total_q=0, max_q_len=0)) == 0
+    assert _plan(b, num_blocks=0) == -1
+    assert _plan(b, num_blocks=-1) == -1
+    # the plan takes no q, caches or output; the run does
+    assert _run(b, q=None) == -1
+    assert _run(b, out=None) == -1
+    assert _plan(b, ws_bytes=64) == -3
+
+
 def test_empty_batch_is_a_no_op():
     # nothing to compute: returns before any HIP call
     assert _attn(_batch(total_q=0, max_q_len=0)) == 0
