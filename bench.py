@@ -299,6 +299,17 @@ def steps_kernel_ms(step, n):
     return [sum(t[i] for t in times) / n for i in range(3)]
 
 
+def paired_kernel_ms(step_a, step_b, n, blocks=4):
+    """Attention kernel ms of `step_a` and of `step_b` (each one attention call), timed in `blocks` alternating
+    runs of n / blocks calls each, so that both see the same clock and cache conditions; returns (a, b)."""
+    per = max(1, n // blocks)
+    ta = tb = 0.0
+    for _ in range(blocks):
+        ta += steps_kernel_ms(step_a, per)[1]
+        tb += steps_kernel_ms(step_b, per)[1]
+    return ta / blocks, tb / blocks
+
+
 def calls_ms(call, n):
     """Average time of n back-to-back calls on the current stream, one event pair around all of them."""
     import torch
@@ -363,7 +374,8 @@ def decode_entry(name, reps):
         raise RuntimeError(f"{name}: kernel error word {dw.decode_error_word():#x}")
     nbytes = metrics.decode_bytes(w)
     _, attn, merge = steps_kernel_ms(dw.decode, reps)
-    prerot = steps_kernel_ms(dw.decode_prerotated, reps)[1]
+    # RoPE overhead: the two kernels in alternating runs of calls
+    attn_p, prerot = paired_kernel_ms(dw.decode, dw.decode_prerotated, reps)
     gbs = nbytes / (attn * 1e-3) / 1e9
     # whole calls (decode kernel + merge) back to back between one pair of events: free of
     # the few microseconds that events around every launch add to such short kernels
@@ -377,7 +389,7 @@ def decode_entry(name, reps):
          "algorithmic_MB": round(nbytes / 1e6, 2), "decode_kernel_ms": round(attn, 5),
          "merge_kernel_ms": round(merge, 5), "GBps_kernel": round(gbs, 1),
          "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2), "prerotated_kernel_ms": round(prerot, 5),
-         "rope_overhead_pct": round(100 * (attn / prerot - 1), 2),
+         "rope_overhead_pct": round(100 * (attn_p / prerot - 1), 2),
          "call_ms_back_to_back": round(call_ms, 5), "prerotated_call_ms_back_to_back": round(call_ms_prerot, 5),
          "GBps_call_back_to_back": round(nbytes / (call_ms * 1e-3) / 1e9, 1),
          "rope_overhead_call_pct": round(100 * (call_ms / call_ms_prerot - 1), 2),
@@ -418,14 +430,15 @@ def suite_entry(name, reps):
         dw.write_new()
         dw.attend_prerotated()
     plan, attn, merge = steps_kernel_ms(step, reps)
-    prerot = steps_kernel_ms(step_prerotated, reps)[1]
+    # RoPE overhead: the two kernels in alternating runs of steps
+    attn_p, prerot = paired_kernel_ms(step, step_prerotated, reps)
     tf = flops / (attn * 1e-3) / 1e12
     e = {"workload": WORKLOADS[name], "query_tokens": int(w.total_q), "gflop": round(flops / 1e9, 3),
          "algorithmic_MB": round(nbytes / 1e6, 1),
          "attention_kernel_ms": round(attn, 5), "plan_kernels_ms": round(plan, 5), "merge_kernel_ms": round(merge, 5),
          "tflops_kernel": round(tf, 2), "pct_mfma_bf16_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2),
          "pct_hbm_peak": round(100 * nbytes / (attn * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
-         "prerotated_kernel_ms": round(prerot, 5), "rope_overhead_pct": round(100 * (attn / prerot - 1), 2)}
+         "prerotated_kernel_ms": round(prerot, 5), "rope_overhead_pct": round(100 * (attn_p / prerot - 1), 2)}
     if name in ("c3", "c3w"):   # shared documents at different offsets
         ms, unique = private_copy_prerotated(dw, w, reps)
         e["prerotated_private_copies_kernel_ms"] = round(ms, 5)
@@ -459,11 +472,11 @@ def sweeps(reps=10):
             dw.attend_prerotated()
         torch.cuda.synchronize()
         plan, attn, merge = steps_kernel_ms(dw.attend, reps)
-        prerot = steps_kernel_ms(dw.attend_prerotated, reps)[1]
+        attn_p, prerot = paired_kernel_ms(dw.attend, dw.attend_prerotated, reps)
         flops = metrics.attention_flops(metrics.workload_pairs(w), w.num_q_heads, w.head_dim)
         rec = {"sweep": sweep, "x": x, "context_tokens": int(L), "query_tokens": int(w.total_q),
                "call_ms": round(plan + attn + merge, 5), "attention_kernel_ms": round(attn, 5),
-               "prerotated_kernel_ms": round(prerot, 5), "rope_overhead_pct": round(100 * (attn / prerot - 1), 2),
+               "prerotated_kernel_ms": round(prerot, 5), "rope_overhead_pct": round(100 * (attn_p / prerot - 1), 2),
                "tflops_kernel": round(flops / (attn * 1e-3) / 1e12, 1), **extra}
         print(json.dumps(rec), flush=True)
         del dw
@@ -563,7 +576,9 @@ def main():
     def step_prerotated():
         dw.write_new()
         dw.attend_prerotated()
-    _, ms_kernel_prerot, _ = steps_kernel_ms(step_prerotated, a.steps)
+    # RoPE overhead: the kernel with and without the rotation in alternating runs of
+    # steps (same clock and cache conditions for both)
+    ms_kernel_paired, ms_kernel_prerot = paired_kernel_ms(dw.step, step_prerotated, a.steps)
     # ---- cold caches: the same steps, each after writing a 512 MB buffer on the
     # stream (more than L2 and the 256 MB Infinity Cache together), so every
     # K/V block, q row and table row comes from HBM; the library's events time
@@ -667,7 +682,8 @@ def main():
             "cold_cache": {"attention_kernel_ms": round(ms_kernel_cold, 5), "plan_kernels_ms": round(ms_plan_cold, 5),
                            "merge_kernel_ms": round(ms_merge_cold, 5),
                            "tflops_attention_kernel": round(flops / (ms_kernel_cold * 1e-3) / 1e12, 2)},
-            "rope_overhead_pct": round(100 * (ms_kernel / ms_kernel_prerot - 1), 2),
+            "rope_overhead_pct": round(100 * (ms_kernel_paired / ms_kernel_prerot - 1), 2),
+            "rope_overhead_note": "in-kernel RoPE against the pre-rotated kernel, both timed in 4 alternating runs of steps",
             "shader_clock_mhz": sclk,
             "pct_hbm_peak_attention_kernel": round(100 * algorithmic_bytes(w) / (ms_kernel * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
             "write_kv_ms": round(ms_wkv, 5),
