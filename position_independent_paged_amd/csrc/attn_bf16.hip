@@ -56,7 +56,9 @@
 //     max). The row sums add the same bf16 P the numerator uses, two at a time
 //     with v_dot2_f32_bf16.
 //   * q rows come in and the output goes out through an LDS row buffer, so
-//     every global load or store instruction moves whole rows.
+//     every global load or store instruction moves whole rows; both are
+//     non-temporal accesses (each byte is touched once), which keeps them
+//     from displacing the K/V lines that the XCD's work-groups share in L2.
 //   * A piece of a split tile stores fp32 (O, m, l) to its slot (O in the
 //     lanes' order); the merge kernel combines the pieces.
 #include "common.h"
@@ -666,8 +668,11 @@ __global__ void __launch_bounds__(64 * kNW, 1) attn_bf16_kernel(AttnParams P) {
         const int rw = 32 * RB * w + RPI * k + ln / CPR;
         const int tq = rw / G;
         const int tq_in = tq < item.nq ? tq : item.nq - 1;
-        qv[k] = *(const u32x4*)((const __bf16*)P.q + (((int64_t)item.row0 + tq_in) * P.hq + g * G + rw % G) * D +
-                                8 * (ln % CPR));
+        // read once: non-temporal, so q does not displace K/V lines that
+        // other work-groups of the XCD still stream through its L2
+        qv[k] = __builtin_nontemporal_load((const u32x4*)((const __bf16*)P.q +
+                                                          (((int64_t)item.row0 + tq_in) * P.hq + g * G + rw % G) * D +
+                                                          8 * (ln % CPR)));
       }
       TokDesc tk[RB];
 #pragma unroll
@@ -918,8 +923,9 @@ __global__ void __launch_bounds__(64 * kNW, 1) attn_bf16_kernel(AttnParams P) {
         const u32x4 v = *(const u32x4*)(rowbuf + (32 * RB * w + rr) * C::KSTR + 8 * (ln % CPR));
         if ((vmask[rr / 32] >> (rr % 32)) & 1u) {
           const int rw = 32 * RB * w + rr;
-          *(u32x4*)((__bf16*)P.out + (((int64_t)item.row0 + rw / G) * P.hq + g * G + rw % G) * D +
-                    8 * (ln % CPR)) = v;
+          // written once and not read by this launch: non-temporal as well
+          __builtin_nontemporal_store(v, (u32x4*)((__bf16*)P.out + (((int64_t)item.row0 + rw / G) * P.hq + g * G + rw % G) * D +
+                                                  8 * (ln % CPR)));
         }
       }
     } else {
