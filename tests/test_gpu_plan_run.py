@@ -103,3 +103,27 @@ def test_run_without_its_plan_computes_nothing():
     dw.attend(out=ref)
     torch.cuda.synchronize()
     assert torch.equal(_bits(out), _bits(ref))
+
+
+def test_plan_beside_write_kv_on_a_second_stream():
+    """The bench's step schedule: planning on a second stream while write_kv runs on
+    the first, then the run on the first stream; every step equals a whole call."""
+    w = workload.make_config("c4_small")
+    dw = stage(w)
+    dw.write_new()
+    ref = torch.empty_like(dw.out)
+    dw.attend(out=ref)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    for rep in range(3):
+        out = torch.full_like(dw.out, float("nan"))
+        cur = torch.cuda.current_stream()
+        side.wait_stream(cur)
+        with torch.cuda.stream(side):
+            dw.plan()
+        dw.write_new()
+        cur.wait_stream(side)
+        dw.run(out=out)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(out), _bits(ref)), f"pass {rep}"
+    assert dw.error_word() == 0
